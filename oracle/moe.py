@@ -1,0 +1,296 @@
+"""fp64 reference of one GPU's routed-expert MoE layer (test infrastructure only).
+
+What is computed (H100-EP page, section 大规模专家并行 / large-scale expert
+parallelism: experts are spread over GPUs and tokens are routed to them, with
+DeepEP doing the dispatch and combine and DeepGEMM doing FP8 grouped GEMMs for
+MoE; GB200 page, sections 怎么做的 / how it is done and 方法实现细节 / method
+details: the FP8 GEMM library quantises and packs input scales, DeepEP shuffles
+tokens to routed experts).  For the rows already dispatched to this GPU:
+
+  S1 count     counts[e] = number of (t, k) with topk_idx[t, k] == e
+  S2 offsets   segment start of each local expert in the permuted buffer
+  S3 rank      stable position of each (t, k) inside its expert's segment
+  S4 permute   a[slot] = x[t], a_scale[slot] = x_scale[t]
+  S5 GEMM1     h = bf16(block-scaled FP8 product of a and W13[e])   (gate/up)
+  S6 act       v = silu(gate) * up, re-quantised to E4M3 with 1x128 scales
+  S7 GEMM2     y = bf16(block-scaled FP8 product of q2 and W2[e])   (down)
+  S8 combine   out[t] = bf16(sum_k topk_w[t, k] * y[slot_of[t, k]])
+
+Readings where the pages are silent (all listed again in the design notes):
+  R1  FP8 = OCP E4M3FN, max 448.
+  R2  scales are fp32; activations carry one scale per 1x128 block along the
+      hidden dimension, weights one per 128x128 block.
+  R3  block scale s = fp32(amax / 448); s = 1 when amax = 0; no epsilon floor.
+  R4  codes q = E4M3_RNE(v / s) with saturation to +-448.
+  R5  W13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
+  R6  activation is SiLU(g) = g * sigmoid(g).
+  R7  h, y and out are stored as bf16 (round to nearest even) from exact sums;
+      the oracle sums in fp64 and rounds once at those three points.
+  R8  rows of one expert are ordered by flat index f = t*K + k (stable).
+  R9  contiguous layout pads every expert segment to a multiple of align_m;
+      masked layout gives expert e the fixed rows [e*C, (e+1)*C).
+  R10 topk_idx == -1 means "not routed to a local expert"; any other id outside
+      [0, E) is skipped and raises status bit 0; rows that do not fit
+      (contiguous: slot >= rows; masked: rank >= C) are dropped in stable
+      order and raise status bit 1.
+  R11 combine sums k in ascending order; a token with no valid row gets 0.
+
+All floating point is float64.  Scales are kept in their natural layout
+(activation scales [rows, H/128], weight scales [E, N/128, K/128]).
+"""
+
+import numpy as np
+
+from .codec import e4m3_decode, e4m3_encode, bf16_round, E4M3_MAX
+
+LAYOUT_CONTIGUOUS = 0
+LAYOUT_MASKED = 1
+STATUS_BAD_EXPERT = 1
+STATUS_OVERFLOW = 2
+BLOCK = 128
+
+
+# --------------------------------------------------------------------------
+# block quantisation (readings R2-R4); used for generated inputs and for S6
+# --------------------------------------------------------------------------
+def quantize_blocks(values, block_rows):
+    """Quantise a 2-D float array to E4M3 codes with per-block fp32 scales.
+
+    Blocks are `block_rows` x 128 (block_rows is 1 for activations, 128 for
+    weights).  For each block: amax = max |v|; s = fp32(amax / 448), or 1 if
+    amax == 0; code = E4M3_RNE(v / s), the quotient taken in fp64 with s as
+    its fp32 value.  Returns (codes uint8 [R, C], scales float32
+    [R / block_rows, C / 128]).
+    """
+    v = np.asarray(values, dtype=np.float64)
+    R, C = v.shape
+    assert R % block_rows == 0 and C % BLOCK == 0
+    blk = v.reshape(R // block_rows, block_rows, C // BLOCK, BLOCK)
+    amax = np.abs(blk).max(axis=(1, 3))
+    s = (amax / E4M3_MAX).astype(np.float32)
+    s = np.where(amax == 0.0, np.float32(1.0), s).astype(np.float32)
+    q = e4m3_encode(blk / s.astype(np.float64)[:, None, :, None])
+    return q.reshape(R, C), s
+
+
+def dequantize_blocks(codes, scales, block_rows):
+    """Inverse view of quantize_blocks: code value times its block's scale."""
+    d = e4m3_decode(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    s = np.repeat(np.repeat(s, block_rows, axis=0), BLOCK, axis=1)
+    return d * s
+
+
+# --------------------------------------------------------------------------
+# S1-S3 layout
+# --------------------------------------------------------------------------
+def dispatch_layout(topk_idx, E, layout, align_m=BLOCK, rows=None, capacity=None):
+    """Count, prefix-sum and stably rank the routed rows (S1-S3; R8-R10).
+
+    topk_idx : int array [T, K] of local expert ids, -1 for "none".
+    layout   : LAYOUT_CONTIGUOUS (needs align_m >= 1 and rows = buffer rows
+               M_cap) or LAYOUT_MASKED (needs capacity C).
+    Returns a dict with
+      counts [E]      rows routed to each expert (before any drop)
+      offsets [E+1]   segment starts; contiguous: prefix sum of counts rounded
+                      up to align_m; masked: e * C
+      slot_of [T, K]  permuted row of each (t, k), -1 if none or dropped
+      row_src [R_tot], row_expert [R_tot]: source token / expert of each
+                      permuted row, -1 for rows that hold no routed entry
+      rows_total      permuted buffer rows (M_cap or E * C)
+      status          bit 0 bad expert id seen, bit 1 row dropped
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    status = 0
+    if np.any(~valid & (flat != -1)):
+        status |= STATUS_BAD_EXPERT
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int64)
+    if layout == LAYOUT_CONTIGUOUS:
+        assert align_m >= 1 and rows is not None
+        padded = -(-counts // align_m) * align_m
+        offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+        rows_total = int(rows)
+    elif layout == LAYOUT_MASKED:
+        assert capacity is not None
+        offsets = np.arange(E + 1, dtype=np.int64) * capacity
+        rows_total = int(E * capacity)
+    else:
+        raise ValueError("unknown layout")
+
+    # stable rank inside each expert: a stable sort by expert id keeps
+    # ascending flat order among equal ids (R8)
+    f_valid = np.nonzero(valid)[0]
+    e_valid = flat[f_valid]
+    order = np.argsort(e_valid, kind="stable")
+    f_sorted = f_valid[order]
+    e_sorted = e_valid[order]
+    first = np.concatenate([[0], np.cumsum(counts)])[:-1]
+    rank = np.arange(len(f_sorted)) - first[e_sorted]
+    slot = offsets[e_sorted] + rank
+    if layout == LAYOUT_CONTIGUOUS:
+        keep = slot < rows_total
+    else:
+        keep = rank < capacity
+    if np.any(~keep):
+        status |= STATUS_OVERFLOW
+
+    slot_of = np.full(T * K, -1, dtype=np.int64)
+    slot_of[f_sorted[keep]] = slot[keep]
+    row_src = np.full(rows_total, -1, dtype=np.int64)
+    row_expert = np.full(rows_total, -1, dtype=np.int64)
+    row_src[slot[keep]] = f_sorted[keep] // K
+    row_expert[slot[keep]] = e_sorted[keep]
+    return dict(counts=counts, offsets=offsets, slot_of=slot_of.reshape(T, K),
+                row_src=row_src, row_expert=row_expert, rows_total=rows_total,
+                status=status)
+
+
+def expert_segments(L):
+    """Valid row range [start, end) of each expert's segment, clipped to the
+    buffer and to the segment (masked experts keep at most C rows)."""
+    offs, counts, R = L["offsets"], L["counts"], L["rows_total"]
+    segs = []
+    for e in range(len(counts)):
+        s = min(int(offs[e]), R)
+        end = min(int(offs[e]) + int(counts[e]), int(offs[e + 1]), R)
+        segs.append((s, max(s, end)))
+    return segs
+
+
+# --------------------------------------------------------------------------
+# S4 permute
+# --------------------------------------------------------------------------
+def permute(x, x_scale, L):
+    """a[slot] = x[row_src[slot]], a_scale[slot] = x_scale[row_src[slot]] for
+    every filled slot; other rows are returned as zero (they are unspecified
+    on the device).  Also returns the boolean mask of filled rows."""
+    src = L["row_src"]
+    filled = src >= 0
+    a = np.zeros((L["rows_total"], x.shape[1]), dtype=np.uint8)
+    sa = np.zeros((L["rows_total"], x_scale.shape[1]), dtype=np.float32)
+    a[filled] = x[src[filled]]
+    sa[filled] = x_scale[src[filled]]
+    return a, sa, filled
+
+
+# --------------------------------------------------------------------------
+# S5 / S7 grouped GEMM
+# --------------------------------------------------------------------------
+def gemm_rows(a_codes, a_scale, w_codes, w_scale):
+    """One expert's block-scaled FP8 product for a set of rows (S5/S7; R2, R7).
+
+    out[m, n] = bf16( sum_k  dec(a[m,k]) * a_scale[m, k//128]
+                            * dec(w[n,k]) * w_scale[n//128, k//128] )
+    with the products and the sum in fp64.  a_codes [M, K], a_scale
+    [M, K/128], w_codes [N, K], w_scale [N/128, K/128].  Returns float64
+    values that are exactly representable in bf16.
+    """
+    A = dequantize_blocks(a_codes, a_scale, 1)
+    B = dequantize_blocks(w_codes, w_scale, BLOCK)
+    return bf16_round(A @ B.T)
+
+
+# --------------------------------------------------------------------------
+# S6 activation + requantisation
+# --------------------------------------------------------------------------
+def silu_mul(h):
+    """v = silu(g) * u with g = h[:, :I] (gate) and u = h[:, I:] (up)
+    (R5, R6), in fp64 on the bf16 values of h."""
+    h = np.asarray(h, dtype=np.float64)
+    I = h.shape[1] // 2
+    g, u = h[:, :I], h[:, I:]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def act_requant(h):
+    """S6: SiLU(gate) * up, then 1x128 block re-quantisation (R3, R4).
+    Returns (q2 codes [M, I], q2_scale fp32 [M, I/128])."""
+    return quantize_blocks(silu_mul(h), 1)
+
+
+# --------------------------------------------------------------------------
+# S8 combine
+# --------------------------------------------------------------------------
+def combine_rows(y_of_slot, slot_of, topk_w, tokens):
+    """out[t] = bf16( sum over k ascending with slot_of[t,k] >= 0 of
+    topk_w[t,k] * y[slot_of[t,k]] ) in fp64 (R11).
+
+    y_of_slot: callable or mapping slot -> float64 row [H].
+    Returns float64 [len(tokens), H] (bf16-representable values).
+    """
+    rows = []
+    for t in tokens:
+        acc = None
+        for k in range(slot_of.shape[1]):
+            s = int(slot_of[t, k])
+            if s < 0:
+                continue
+            term = np.float64(topk_w[t, k]) * y_of_slot[s]
+            acc = term if acc is None else acc + term
+        rows.append(acc)
+    H = next((r.shape[0] for r in rows if r is not None), None)
+    out = np.zeros((len(tokens), H if H is not None else 0))
+    for i, r in enumerate(rows):
+        if r is not None:
+            out[i] = bf16_round(r)
+    return out
+
+
+# --------------------------------------------------------------------------
+# chained layer (optionally on a subset of source tokens)
+# --------------------------------------------------------------------------
+def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
+          align_m=BLOCK, rows=None, capacity=None, tokens=None):
+    """Run S1-S8 on the CPU.
+
+    x [T, H] E4M3 codes, x_scale [T, H/128]; w13 [E, 2I, H], s13
+    [E, 2I/128, H/128]; w2 [E, H, I], s2 [E, H/128, I/128]; topk_idx /
+    topk_w [T, K].  With `tokens` given, only those tokens' rows go through
+    S5-S8 (each routed row depends only on its own source token, so the
+    result for those tokens is exactly the full layer's).
+
+    Returns a dict: the layout, `slots` (the permuted rows computed), and for
+    those rows `h` [n, 2I], `q2` [n, I], `q2_scale` [n, I/128], `y` [n, H]
+    (float64 bf16 values / uint8 codes), plus `tokens` and `out`
+    [len(tokens), H].
+    """
+    E = w13.shape[0]
+    T = x.shape[0]
+    L = dispatch_layout(topk_idx, E, layout, align_m, rows, capacity)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    so = L["slot_of"][tokens]
+    slots = np.unique(so[so >= 0])
+    I = w13.shape[1] // 2
+    H = x.shape[1]
+    h = np.zeros((len(slots), 2 * I))
+    q2 = np.zeros((len(slots), I), dtype=np.uint8)
+    q2s = np.zeros((len(slots), I // BLOCK), dtype=np.float32)
+    y = np.zeros((len(slots), H))
+    ex = L["row_expert"][slots]
+    src = L["row_src"][slots]
+    for e in range(E):
+        sel = np.nonzero(ex == e)[0]
+        if len(sel) == 0:
+            continue
+        xa, xs = x[src[sel]], x_scale[src[sel]]
+        h[sel] = gemm_rows(xa, xs, w13[e], s13[e])
+        q, qs = act_requant(h[sel])
+        q2[sel], q2s[sel] = q, qs
+        y[sel] = gemm_rows(q, qs, w2[e], s2[e])
+    pos = {int(s): i for i, s in enumerate(slots)}
+    y_of_slot = {s: y[i] for s, i in pos.items()}
+    out = combine_rows(y_of_slot, L["slot_of"], topk_w, tokens)
+    if out.shape[1] == 0:
+        out = np.zeros((len(tokens), H))
+    return dict(layout=L, slots=slots, h=h, q2=q2, q2_scale=q2s, y=y,
+                tokens=tokens, out=out)
+
+
+def layer_flops(counts_valid, H, I):
+    """Algorithmic FLOPs of S5 + S7 for the given number of valid rows."""
+    R = int(np.sum(counts_valid))
+    return 2 * R * (2 * I) * H + 2 * R * H * I
