@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of one MI355X's share of the FP8 routed-expert MoE layer.
+
+A step is one pass of the whole hot path over one batch of routed rows:
+count / prefix-sum / stable-rank / permute (moe_dispatch_layout), FP8 grouped
+GEMM gate/up, SiLU-mul-requant, FP8 grouped GEMM down, weighted combine.
+Default workload: the prefill share of an EP32 deployment at 4K context (9
+local experts of a 288-expert pool, H=7168, I=2048, 65,536 source tokens,
+top-8, 131,040 routed rows, contiguous layout).  Inputs are synthetic
+(seeded), quantised on the device by the library's own quantiser and
+resident in HBM before timing starts.
+
+Prints one JSON line: MoE-layer FP8 TFLOP/s (value), token-rows/s, the
+fraction of the FP8 MFMA peak, per-kernel times, the roofline of the dominant
+kernel (GEMM1, events on the launch stream) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE-layer FP8 TFLOP/s + % of MFMA peak; routed token-rows/s per GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_ep32_prefill_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "fp8_routed_expert_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_source_hash():
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(launch_key):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 --pmc summary,
+    or None when that summary is absent or was taken on another kernel."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha") != gemm_source_hash() or rec.get("launch") != launch_key:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, idx, w, n_tokens):
+    """Time the CPU oracle (as it stands) on a seeded sample of source tokens.
+
+    The sample's activations and all experts' weights are quantised by the
+    oracle itself (untimed); the timed call is the oracle's layer: the layout
+    over all tokens and the float stages for the sampled tokens' rows."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_info
+    from oracle import moe
+    from workloads import activations, weights, bf16_to_f32
+
+    g = np.random.default_rng([0, cfg.cid, 99])
+    toks = np.sort(g.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    xb = activations(cfg)
+    x = np.zeros((cfg.T, cfg.H), np.uint8)
+    xs = np.ones((cfg.T, cfg.H // 128), np.float32)
+    x[toks], xs[toks] = moe.quantize_blocks(bf16_to_f32(xb[toks]), 1)
+    E = cfg.E
+    w13 = np.empty((E, 2 * cfg.I, cfg.H), np.uint8)
+    s13 = np.empty((E, 2 * cfg.I // 128, cfg.H // 128), np.float32)
+    w2 = np.empty((E, cfg.H, cfg.I), np.uint8)
+    s2 = np.empty((E, cfg.H // 128, cfg.I // 128), np.float32)
+
+    def qe(e):
+        a, b = weights(cfg, experts=[e])
+        w13[e], s13[e] = moe.quantize_blocks(bf16_to_f32(a[0]), 128)
+        w2[e], s2[e] = moe.quantize_blocks(bf16_to_f32(b[0]), 128)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(qe, range(E)))
+    rows = int((idx >= 0).sum()) + E * (cfg.align_m - 1)
+    kw = dict(capacity=cfg.capacity) if cfg.layout == moe.LAYOUT_MASKED else \
+        dict(align_m=cfg.align_m, rows=rows)
+    t0 = time.perf_counter()
+    res = moe.layer(x, xs, idx, w, w13, s13, w2, s2, cfg.layout, tokens=toks, **kw)
+    dt = time.perf_counter() - t0
+    n_rows = len(res["slots"])
+    flops = 2 * n_rows * (2 * cfg.I) * cfg.H + 2 * n_rows * cfg.H * cfg.I
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.T} source tokens ({n_rows} routed rows), seeded; "
+                      f"layout over all tokens; fp64 numpy, BLAS threads={threads}",
+            "seconds": round(dt, 3), "rows_per_s": n_rows / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="source tokens in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the expert-parallel layer; "
+              "runs on more than one GPU are not part of this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import fp8_routed_expert_amd as fre
+    from workloads import CONFIGS, routing, activations, weights
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"workload {cfg.name}: E={cfg.E} H={cfg.H} I={cfg.I} T={cfg.T} K={cfg.K}")
+    idx, w = routing(cfg)
+    R = int((idx >= 0).sum())
+    xb = activations(cfg)
+    w13b, w2b = weights(cfg)
+    log(f"generated inputs ({R} routed rows)")
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    E, H, I, T, K = cfg.E, cfg.H, cfg.I, cfg.T, cfg.K
+    x = torch.empty(T, H, dtype=torch.uint8, device=dev)
+    xs = torch.empty(T, H // 128, dtype=torch.float32, device=dev)
+    w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=dev)
+    s13 = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=dev)
+    s2 = torch.empty(E, H // 128, I // 128, dtype=torch.float32, device=dev)
+    fre.moe_quantize_fp8(bf(xb), 1, x, xs)
+    fre.moe_quantize_fp8(bf(w13b), 128, w13, s13)
+    fre.moe_quantize_fp8(bf(w2b), 128, w2, s2)
+    del xb, w13b, w2b
+    idx_d = torch.from_numpy(idx).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
+    rows = cfg.capacity if cfg.layout == fre.LAYOUT_MASKED else fre.contiguous_rows(R, E, cfg.align_m)
+    layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        layer.dispatch(idx_d, x, xs)
+        if evs is not None:
+            evs[1].record()
+        layer.gemm1(w13, s13)
+        if evs is not None:
+            evs[2].record()
+        layer.act()
+        if evs is not None:
+            evs[3].record()
+        layer.gemm2(w2, s2)
+        if evs is not None:
+            evs[4].record()
+        layer.combine(w_d)
+        if evs is not None:
+            evs[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = int(layer.status.item())
+    if st != 0:
+        raise RuntimeError(f"device status word {st} after warm-up")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    names = ["dispatch_layout", "gemm1_gate_up", "act_requant", "gemm2_down", "combine"]
+    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
+                             for k in range(args.steps)])) for i, n in enumerate(names)}
+
+    flops1 = 2.0 * R * (2 * I) * H
+    flops2 = 2.0 * R * H * I
+    flops = flops1 + flops2
+    hb = H // 128
+    bytes_perm = (T + R) * (H + 4 * hb) + T * K * 4
+    bytes_act = R * (4 * I + I + 4 * (I // 128))
+    bytes_comb = R * 2 * H + T * 2 * H + T * K * 8
+    tflops = flops / (ms * 1e-3) / 1e12
+    g1 = flops1 / (per["gemm1_gate_up"] * 1e-3) / 1e12
+    launch_key = f"{cfg.name}:R={R}:rows={rows}"
+    traffic = stored_traffic(launch_key)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {E} local experts, H={H}, I={I}, "
+                               f"{T} source tokens, top-{K}, {R} routed rows, "
+                               f"{'masked' if cfg.layout else 'contiguous'} layout",
+                   "experts": E, "hidden": H, "intermediate": I, "tokens": T,
+                   "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total},
+        "mfma_peak_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "token_rows_per_s": round(R / (ms * 1e-3), 1),
+        "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "per_kernel_rate": {
+            "gemm1_tflops": round(g1, 1),
+            "gemm2_tflops": round(flops2 / (per["gemm2_down"] * 1e-3) / 1e12, 1),
+            "dispatch_gbs": round(bytes_perm / (per["dispatch_layout"] * 1e-3) / 1e9, 1),
+            "act_gbs": round(bytes_act / (per["act_requant"] * 1e-3) / 1e9, 1),
+            "combine_gbs": round(bytes_comb / (per["combine"] * 1e-3) / 1e9, 1),
+        },
+        "roofline": {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "mfma",
+                     "achieved": round(g1, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g1 / FP8_PEAK_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, idx, w, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

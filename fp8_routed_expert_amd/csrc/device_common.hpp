@@ -1,0 +1,78 @@
+// Device-side helpers shared by the gfx950 kernels of libmoe_fp8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_fp8.h"
+
+namespace moe {
+
+constexpr int kBlock = 128;       // scale block width (1x128 / 128x128)
+constexpr float kE4M3Max = 448.0f;
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Saturate to the E4M3 range; NaN passes through (comparisons are false).
+__device__ __forceinline__ float sat_e4m3(float v) {
+  v = v > kE4M3Max ? kE4M3Max : v;
+  v = v < -kE4M3Max ? -kE4M3Max : v;
+  return v;
+}
+
+// Two fp32 values -> two E4M3 codes in the low 16 bits (a in byte 0, b in
+// byte 1).  The gfx950 conversion rounds to nearest even in the default
+// rounding mode; inputs are saturated first so no out-of-range value
+// reaches it.
+__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b) {
+  return static_cast<uint32_t>(
+             __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false)) &
+         0xffffu;
+}
+
+// Reductions over aligned groups of 16 lanes (one 128-wide block held as
+// 8 values per lane).
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  return v;
+}
+
+// Block scale for a 128-wide block with absolute maximum amax (>= 0).
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+}
+
+// Valid row range of expert e: [start, end) inside the segment and buffer.
+// Returns false (and flags) when the segment description is outside the
+// buffer; the range is then clipped so callers never index out of bounds.
+__device__ __forceinline__ void expert_rows(const int32_t* offsets,
+                                            const int32_t* counts, int e,
+                                            int rows_total, int& start,
+                                            int& end) {
+  int o0 = offsets[e];
+  int o1 = offsets[e + 1];
+  int c = counts[e];
+  long long s = o0 < 0 ? 0 : o0;
+  if (s > rows_total) s = rows_total;
+  long long lim = (long long)o0 + (c < 0 ? 0 : c);
+  if (lim > o1) lim = o1;
+  if (lim > rows_total) lim = rows_total;
+  if (lim < s) lim = s;
+  start = (int)s;
+  end = (int)lim;
+}
+
+}  // namespace moe

@@ -1,0 +1,76 @@
+"""A routed-expert MoE layer share that owns its device buffers.
+
+MoELayer allocates every intermediate once (torch device memory) and runs
+the five library calls of one layer on a stream:
+
+  moe_dispatch_layout -> moe_grouped_gemm_fp8 (gate/up) -> moe_act_requant
+  -> moe_grouped_gemm_fp8 (down) -> moe_combine
+
+All arithmetic happens in the HIP library; this class only holds memory.
+The call sequence allocates nothing and reads nothing back, so it can be
+captured into a hipGraph (torch.cuda.CUDAGraph) and replayed.
+"""
+
+import torch
+
+from . import ops
+
+
+def contiguous_rows(R, E, align_m=128):
+    """Buffer rows that hold R routed rows in E segments aligned to align_m."""
+    return int(R) + E * (align_m - 1)
+
+
+class MoELayer:
+    def __init__(self, E, H, I, T, K, layout, rows, align_m=128, device="cuda"):
+        """rows: M_cap for the contiguous layout, capacity C for masked."""
+        self.E, self.H, self.I, self.T, self.K = E, H, I, T, K
+        self.layout, self.rows, self.align_m = layout, rows, align_m
+        self.rows_total = E * rows if layout == ops.LAYOUT_MASKED else rows
+        R, d = self.rows_total, device
+        i32 = dict(dtype=torch.int32, device=d)
+        self.counts = torch.zeros(E, **i32)
+        self.offsets = torch.zeros(E + 1, **i32)
+        self.slot_of = torch.zeros(T, K, **i32)
+        self.row_src = torch.zeros(R, **i32)
+        self.row_expert = torch.zeros(R, **i32)
+        self.a = torch.zeros(R, H, dtype=torch.uint8, device=d)
+        self.a_scale = torch.zeros(H // 128, R, dtype=torch.float32, device=d)
+        self.h = torch.zeros(R, 2 * I, dtype=torch.bfloat16, device=d)
+        self.q2 = torch.zeros(R, I, dtype=torch.uint8, device=d)
+        self.q2_scale = torch.zeros(I // 128, R, dtype=torch.float32, device=d)
+        self.y = torch.zeros(R, H, dtype=torch.bfloat16, device=d)
+        self.out = torch.zeros(T, H, dtype=torch.bfloat16, device=d)
+        self.workspace = torch.zeros(max(1, ops.moe_layout_workspace_bytes(T, K, E)),
+                                     dtype=torch.uint8, device=d)
+        self.status = torch.zeros(1, **i32)
+
+    def dispatch(self, topk_idx, x, x_scale, stream=None):
+        ops.moe_dispatch_layout(topk_idx, x, x_scale, self.E, self.layout, self.align_m,
+                                self.rows, self.counts, self.offsets, self.slot_of,
+                                self.row_src, self.row_expert, self.a, self.a_scale,
+                                self.workspace, self.status, stream)
+
+    def gemm1(self, w13, s13, stream=None):
+        ops.moe_grouped_gemm_fp8(self.a, self.a_scale, w13, s13, self.offsets, self.counts,
+                                 self.h, self.status, stream)
+
+    def act(self, stream=None):
+        ops.moe_act_requant(self.h, self.offsets, self.counts, self.q2, self.q2_scale,
+                            self.status, stream)
+
+    def gemm2(self, w2, s2, stream=None):
+        ops.moe_grouped_gemm_fp8(self.q2, self.q2_scale, w2, s2, self.offsets, self.counts,
+                                 self.y, self.status, stream)
+
+    def combine(self, topk_w, stream=None):
+        ops.moe_combine(self.y, self.slot_of, topk_w, self.out, self.status, stream)
+
+    def forward(self, topk_idx, x, x_scale, topk_w, w13, s13, w2, s2, stream=None):
+        """One full pass S1-S8; returns self.out (bf16 [T, H])."""
+        self.dispatch(topk_idx, x, x_scale, stream)
+        self.gemm1(w13, s13, stream)
+        self.act(stream)
+        self.gemm2(w2, s2, stream)
+        self.combine(topk_w, stream)
+        return self.out

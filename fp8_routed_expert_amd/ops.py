@@ -1,0 +1,135 @@
+"""Python binding of libmoe_fp8: one function per C entry point, same names.
+
+Each function checks shapes, dtypes, devices and contiguity of the torch
+tensors it is given, then passes their device pointers and the current HIP
+stream to the library.  Nothing is computed here.  FP8 tensors are
+torch.uint8 (or torch.float8_e4m3fn, passed as bytes); bf16 tensors are
+torch.bfloat16; scales float32; indices int32.
+"""
+
+import torch
+
+from ._lib import load, check
+
+LAYOUT_CONTIGUOUS = 0
+LAYOUT_MASKED = 1
+ERR_BAD_EXPERT = 1
+ERR_OVERFLOW = 2
+ERR_BAD_INDEX = 4
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t, dtypes, name, shape=None):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.data_ptr()
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def moe_layout_workspace_bytes(T, K, E):
+    return int(load().moe_layout_workspace_bytes(T, K, E))
+
+
+def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
+                        offsets, slot_of, row_src, row_expert, a, a_scale,
+                        workspace, status, stream=None):
+    """Count / prefix-sum / stably rank / permute the routed rows.
+
+    rows is M_cap (contiguous) or the per-expert capacity C (masked);
+    a is [rows_total, H], a_scale [H/128, rows_total] (K-block-major)."""
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    rows_total = E * rows if layout == LAYOUT_MASKED else rows
+    lib = load()
+    st = lib.moe_dispatch_layout(
+        _ptr(topk_idx, _I32, "topk_idx", (T, K)), _ptr(x, _U8, "x", (T, H)),
+        _ptr(x_scale, _F32, "x_scale", (T, H // 128)), T, K, E, H, layout,
+        align_m, rows, _ptr(counts, _I32, "counts", (E,)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)),
+        _ptr(slot_of, _I32, "slot_of", (T, K)),
+        _ptr(row_src, _I32, "row_src", (rows_total,)),
+        _ptr(row_expert, _I32, "row_expert", (rows_total,)),
+        _ptr(a, _U8, "a", (rows_total, H)),
+        _ptr(a_scale, _F32, "a_scale", (H // 128, rows_total)),
+        _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_dispatch_layout")
+
+
+def moe_grouped_gemm_fp8(a, a_scale, w, w_scale, offsets, counts, c, status,
+                         stream=None):
+    """c[valid rows] = block-scaled FP8 grouped GEMM of a with w[expert]."""
+    E, N, K = w.shape
+    rows_total = a.shape[0]
+    lib = load()
+    st = lib.moe_grouped_gemm_fp8(
+        _ptr(a, _U8, "a", (rows_total, K)),
+        _ptr(a_scale, _F32, "a_scale", (K // 128, rows_total)),
+        _ptr(w, _U8, "w", (E, N, K)),
+        _ptr(w_scale, _F32, "w_scale", (E, N // 128, K // 128)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)), _ptr(counts, _I32, "counts", (E,)),
+        E, rows_total, N, K, _ptr(c, _BF16, "c", (rows_total, N)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_grouped_gemm_fp8")
+
+
+def moe_act_requant(h, offsets, counts, q, q_scale, status, stream=None):
+    """q, q_scale = E4M3 1x128 requantisation of silu(h[:, :I]) * h[:, I:]."""
+    rows_total, I2 = h.shape
+    I = I2 // 2
+    E = counts.numel()
+    lib = load()
+    st = lib.moe_act_requant(
+        _ptr(h, _BF16, "h"), _ptr(offsets, _I32, "offsets", (E + 1,)),
+        _ptr(counts, _I32, "counts", (E,)), E, rows_total, I,
+        _ptr(q, _U8, "q", (rows_total, I)),
+        _ptr(q_scale, _F32, "q_scale", (I // 128, rows_total)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_act_requant")
+
+
+def moe_combine(y, slot_of, topk_w, out, status, stream=None):
+    """out[t] = sum_k topk_w[t,k] * y[slot_of[t,k]] (bf16, fp32 accumulation)."""
+    rows_total, H = y.shape
+    T, K = slot_of.shape
+    lib = load()
+    st = lib.moe_combine(
+        _ptr(y, _BF16, "y"), rows_total, _ptr(slot_of, _I32, "slot_of"),
+        _ptr(topk_w, _F32, "topk_w", (T, K)), T, K, H,
+        _ptr(out, _BF16, "out", (T, H)), _ptr(status, _I32, "status", (1,)),
+        _stream(stream))
+    check(st, "moe_combine")
+
+
+def moe_quantize_fp8(x, block_rows, q, scale, stream=None):
+    """E4M3 block quantisation of a bf16 or fp32 [rows, cols] tensor (or a
+    stacked [E, N, K] weight, taken as rows = E*N) with 1x128 or 128x128
+    blocks."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    is_f32 = x.dtype == torch.float32
+    if q.numel() != x.numel() or scale.numel() != rows // block_rows * (cols // 128):
+        raise ValueError("moe_quantize_fp8: q / scale sizes do not match x")
+    lib = load()
+    st = lib.moe_quantize_fp8(
+        _ptr(x, _BF16 + _F32, "x"), 1 if is_f32 else 0, rows, cols, block_rows,
+        _ptr(q, _U8, "q"), _ptr(scale, _F32, "scale"), _stream(stream))
+    check(st, "moe_quantize_fp8")

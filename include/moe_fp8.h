@@ -1,0 +1,213 @@
+/*
+ * moe_fp8.h — C ABI of the MI355X (gfx950) FP8 routed-expert MoE library.
+ *
+ * One GPU's share of a routed-expert MoE layer under expert parallelism: the
+ * token-rows already dispatched to this GPU's local experts are counted per
+ * expert, prefix-summed and permuted (the receive side of DeepEP's token
+ * shuffle), pushed through two FP8 grouped GEMMs with a SiLU-gated
+ * re-quantisation between them (the DeepGEMM grouped GEMMs), and summed back
+ * per source token with their top-k weights (the combine).
+ *
+ * Sources:
+ *   [H100-EP] "Deploying DeepSeek with PD Disaggregation and Large-Scale
+ *             Expert Parallelism on 96 H100 GPUs", section 大规模专家并行
+ *             (large-scale expert parallelism): subsections 基于 DeepEP 的
+ *             专家并行 (DeepEP dispatch/combine; normal mode for prefill,
+ *             low-latency CUDA-graph-compatible mode for decode, and the
+ *             mode-compatibility table) and DeepGEMM 集成 (two FP8 grouped
+ *             GEMM functions for MoE, one per inference phase).
+ *   [GB200]   "Deploying DeepSeek on GB200 NVL72 with PD and Large Scale EP
+ *             (Part I): 2.7x Higher Decoding Throughput", sections 怎么做的
+ *             (how it is done) and 方法实现细节 (method details): FP8 GEMM
+ *             library whose API quantises and packs input scales; DeepEP
+ *             shuffles tokens to routed experts.
+ * The pages give no kernel-level definitions; block sizes, rounding and the
+ * activation are readings, stated with each call.
+ *
+ * Conventions for every call
+ *   - All array arguments are device pointers to caller-owned memory; the
+ *     library never allocates, frees or synchronises, and keeps no pointer
+ *     after returning.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the legacy default stream).  Every call is safe inside hipGraph stream
+ *     capture (fixed grids, no host reads of device data, no memset nodes).
+ *   - FP8 is OCP E4M3FN (max 448), stored one byte per value.  bf16 is stored
+ *     as uint16_t bit patterns.  Scales are fp32.
+ *   - Activation scales live K-block-major ("MN-major"): for a buffer of
+ *     `rows` rows and hidden size H the scale of row m, block kb (covering
+ *     columns [128 kb, 128 kb + 128)) is at scale[kb * rows + m].  Source
+ *     activation scales (x_scale) are row-major [T, H/128].  Weight scales
+ *     are [E, N/128, K/128] row-major, one per 128x128 block.
+ *   - Matrices are row-major; weights are [E, N, K] with K contiguous.
+ *   - Pointers must be 16-byte aligned; H, I, N, K must be multiples of 128.
+ *   - Host-side argument errors return a non-zero moe_status_t and launch
+ *     nothing.  Data errors found on the device (bad expert id, a row that
+ *     does not fit, an index outside a buffer) are OR-ed into the caller's
+ *     int32 word *status_dev (caller zeroes it; the library never reads it
+ *     back) and the offending entry is skipped deterministically.
+ *   - A valid permuted row is one inside an expert segment: rows
+ *     [offsets[e], offsets[e] + min(counts[e], offsets[e+1] - offsets[e]))
+ *     clipped to the buffer.  Outputs for other rows are unspecified.
+ */
+#ifndef MOE_FP8_H_
+#define MOE_FP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+
+#define MOE_OK 0
+#define MOE_INVALID_ARG 1       /* null pointer, negative size, bad enum   */
+#define MOE_UNSUPPORTED_SHAPE 2 /* size not a multiple of 128, misaligned   */
+#define MOE_HIP_ERROR 3         /* a kernel launch failed                   */
+
+#define MOE_LAYOUT_CONTIGUOUS 0 /* prefill: expert segments stacked along M */
+#define MOE_LAYOUT_MASKED 1     /* decode: fixed [E, C, .] + device counts  */
+
+/* bits OR-ed into *status_dev */
+#define MOE_ERR_BAD_EXPERT 1 /* topk id outside [-1, E): entry skipped     */
+#define MOE_ERR_OVERFLOW 2   /* row did not fit: dropped in stable order  */
+#define MOE_ERR_BAD_INDEX 4  /* slot / offset outside a buffer: skipped   */
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+
+/* ABI version of this header (increments on any signature change). */
+int moe_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* moe_status_string(moe_status_t status);
+
+/* Bytes of device workspace moe_dispatch_layout needs for T tokens with K
+ * top-k columns and E local experts (per-chunk expert histograms). */
+size_t moe_layout_workspace_bytes(int T, int K, int E);
+
+/*
+ * moe_dispatch_layout — count, prefix-sum, stably rank and permute the
+ * routed rows (steps: count per expert, prefix sum, permute) [H100-EP
+ * 基于 DeepEP 的专家并行: tokens are routed to the experts that own them;
+ * normal mode feeds prefill (contiguous layout), low-latency mode feeds
+ * decode inside a graph (masked layout)].
+ *
+ *   topk_idx  [T, K] int32   local expert id per (token, pick), -1 = none
+ *   x         [T, H] e4m3    source activations
+ *   x_scale   [T, H/128] f32 their 1x128 block scales (row-major)
+ *   layout    MOE_LAYOUT_CONTIGUOUS or MOE_LAYOUT_MASKED
+ *   align_m   contiguous: every expert segment is padded to a multiple of
+ *             align_m rows (>= 1); ignored for masked
+ *   rows      contiguous: rows of the permuted buffer (M_cap);
+ *             masked: capacity C rows per expert (buffer has E*C rows)
+ * Outputs (rows_total = rows for contiguous, E*C for masked):
+ *   counts    [E]      rows routed to each expert (before drops)
+ *   offsets   [E+1]    segment starts: contiguous = prefix sum of counts
+ *                      rounded up to align_m; masked = e*C
+ *   slot_of   [T, K]   permuted row of each (t, k); -1 = none / dropped
+ *   row_src   [rows_total]  source token of each row, -1 if no entry
+ *   row_expert[rows_total]  expert of each row, -1 if no entry
+ *   a         [rows_total, H] e4m3   a[slot] = x[row_src[slot]]
+ *   a_scale   [H/128, rows_total] f32 (K-block-major) matching scales
+ *   workspace moe_layout_workspace_bytes(T, K, E) bytes of device memory
+ * Rows of one expert are ordered by flat index t*K + k.  Rows that do not
+ * fit (contiguous: slot >= rows; masked: rank >= C) are dropped and set
+ * MOE_ERR_OVERFLOW; ids outside [-1, E) are skipped and set
+ * MOE_ERR_BAD_EXPERT.  Rows of `a` / `a_scale` holding no entry are left
+ * untouched.
+ */
+moe_status_t moe_dispatch_layout(const int32_t* topk_idx, const uint8_t* x,
+                                 const float* x_scale, int T, int K, int E,
+                                 int H, int layout, int align_m, int rows,
+                                 int32_t* counts, int32_t* offsets,
+                                 int32_t* slot_of, int32_t* row_src,
+                                 int32_t* row_expert, uint8_t* a,
+                                 float* a_scale, void* workspace,
+                                 size_t workspace_bytes, int32_t* status_dev,
+                                 void* stream);
+
+/*
+ * moe_grouped_gemm_fp8 — block-scaled FP8 grouped GEMM over the expert
+ * segments [H100-EP DeepGEMM 集成: FP8 grouped GEMMs for MoE; GB200 方法实现
+ * 细节: FP8 GEMM whose API takes quantised input scales].  For every valid
+ * row m of expert e and every n in [0, N):
+ *
+ *   c[m, n] = bf16_rne( sum_kb  a_scale[kb, m] * w_scale[e, n/128, kb]
+ *                               * sum_{k in block kb} a[m, k] * w[e, n, k] )
+ *
+ * with fp32 accumulation (the 128-wide inner sums are exact products of
+ * E4M3 values summed in fp32 by the matrix cores; the scales are applied in
+ * fp32 once per 128-column block).  Used twice per layer: gate/up
+ * (N = 2I, K = H; rows [0, I) of w are the gate, [I, 2I) the up projection)
+ * and down (N = H, K = I).
+ *
+ *   a        [rows_total, K] e4m3      a_scale [K/128, rows_total] f32
+ *   w        [E, N, K] e4m3            w_scale [E, N/128, K/128] f32
+ *   offsets  [E+1], counts [E] int32 on the device (from moe_dispatch_layout)
+ *   c        [rows_total, N] bf16; only valid rows are written
+ * Segments outside the buffer are clipped and set MOE_ERR_BAD_INDEX.
+ */
+moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
+                                  const uint8_t* w, const float* w_scale,
+                                  const int32_t* offsets,
+                                  const int32_t* counts, int E,
+                                  int rows_total, int N, int K, uint16_t* c,
+                                  int32_t* status_dev, void* stream);
+
+/*
+ * moe_act_requant — SiLU(gate) * up, re-quantised to E4M3 with fresh 1x128
+ * scales (reading: SiLU and the gate/up order are not on the pages).  For
+ * every valid row m and j in [0, I):
+ *   v = silu(h[m, j]) * h[m, I + j],  silu(g) = g / (1 + exp(-g))  (fp32)
+ *   per block jb of 128 columns: s = amax|v| / 448 (1 if amax == 0)
+ *   q[m, j] = e4m3_rne(clamp(v / s, -448, 448)); q_scale[jb, m] = s
+ *
+ *   h        [rows_total, 2I] bf16
+ *   q        [rows_total, I] e4m3     q_scale [I/128, rows_total] f32
+ */
+moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
+                             const int32_t* counts, int E, int rows_total,
+                             int I, uint8_t* q, float* q_scale,
+                             int32_t* status_dev, void* stream);
+
+/*
+ * moe_combine — un-permute and sum each token's rows weighted by its top-k
+ * weights [H100-EP 基于 DeepEP 的专家并行: combine returns expert outputs to
+ * their source tokens]:
+ *   out[t, :] = bf16_rne( sum_{k = 0..K-1, slot_of[t,k] >= 0}
+ *                          topk_w[t, k] * y[slot_of[t, k], :] )
+ * accumulated in fp32 in ascending k; a token with no valid row gets 0.
+ * Deterministic (gather, no atomics).
+ *
+ *   y        [rows_total, H] bf16
+ *   slot_of  [T, K] int32; topk_w [T, K] f32
+ *   out      [T, H] bf16
+ * Slots >= rows_total are skipped and set MOE_ERR_BAD_INDEX.
+ */
+moe_status_t moe_combine(const uint16_t* y, int rows_total,
+                         const int32_t* slot_of, const float* topk_w, int T,
+                         int K, int H, uint16_t* out, int32_t* status_dev,
+                         void* stream);
+
+/*
+ * moe_quantize_fp8 — source-side block quantisation to E4M3 [GB200 方法实现
+ * 细节: the FP8 GEMM API quantises the input scales].  Produces the inputs
+ * the layer consumes: activations with one scale per 1x128 block
+ * (block_rows = 1, scale [rows, cols/128] row-major) and weights with one
+ * scale per 128x128 block (block_rows = 128, scale [rows/128, cols/128];
+ * stacked expert weights [E, N, K] are rows = E*N).  Per block:
+ *   s = amax|x| / 448 (1 if amax == 0);  q = e4m3_rne(clamp(x / s, +-448)).
+ *
+ *   x        [rows, cols], bf16 (x_is_f32 = 0) or f32 (x_is_f32 = 1)
+ *   q        [rows, cols] e4m3, scale as above
+ */
+moe_status_t moe_quantize_fp8(const void* x, int x_is_f32, int rows, int cols,
+                              int block_rows, uint8_t* q, float* scale,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H_ */

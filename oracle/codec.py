@@ -69,19 +69,21 @@ def e4m3_encode(v):
 
 
 def _e4m3_encode(v):
-    r = e4m3_round(v)
-    mag = np.abs(r)
-    nan = np.isnan(r)
-    mag = np.where(nan, 0.0, mag)
-    _, ex = np.frexp(mag)
-    normal = mag >= 2.0 ** -6
-    # normal: mag = 2^(ex-1) * (1 + m/8), exponent field = ex - 1 + 7
-    efield = np.where(normal, ex + 6, 0)
-    mfield = np.where(normal,
-                      np.ldexp(mag, (1 - ex).astype(np.int32)) * 8.0 - 8.0,
-                      np.ldexp(mag, 9))
-    code = (np.signbit(r).astype(np.int64) << 7) | (efield.astype(np.int64) << 3) \
-        | np.rint(mfield).astype(np.int64)
+    # With a = min(|v|, 448) in binade 2^(x-1) <= a < 2^x and b = max(x, -5)
+    # (b = -5 covers the subnormals and the lowest normal binade, which share
+    # spacing 2^-9), the rounded magnitude is q * 2^(b-4) with integer
+    # q = rint(a * 2^(4-b)) in [0, 16].  Its code is 8*b + 40 + q: for b > -5
+    # that is exponent field b+6 and mantissa q-8 (q = 16 carries into the
+    # next exponent with mantissa 0); for b = -5 it is q itself, which is the
+    # subnormal code for q < 8 and the normal code for q >= 8.
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    nan = np.isnan(v)
+    a = np.where(nan, 0.0, a)
+    _, ex = np.frexp(a)
+    b = np.maximum(ex, -5)
+    q = np.rint(np.ldexp(a, 4 - b)).astype(np.int64)
+    mag_code = np.where(a == 0.0, 0, 8 * b.astype(np.int64) + 40 + q)
+    code = (np.signbit(v).astype(np.int64) << 7) | mag_code
     code = np.where(nan, E4M3_NAN_CODE, code)
     return code.astype(np.uint8)
 

@@ -1,0 +1,86 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/moe_fp8.h declares, and rejects bad host-side arguments before any
+launch (nothing here touches a GPU)."""
+
+import ctypes
+
+import pytest
+
+from fp8_routed_expert_amd import _lib
+
+
+def test_library_exports_every_header_function():
+    lib = _lib.load()
+    names = _lib.header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.moe_abi_version() == _lib.ABI_VERSION
+    for s in range(4):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    # one int32 histogram and one int32 base per (chunk of 4096 entries, expert)
+    assert lib.moe_layout_workspace_bytes(65536, 8, 9) == 2 * 128 * 9 * 4
+    assert lib.moe_layout_workspace_bytes(1, 1, 4) == 2 * 1 * 4 * 4
+    assert lib.moe_layout_workspace_bytes(0, 8, 4) == 2 * 1 * 4 * 4
+    assert lib.moe_layout_workspace_bytes(-1, 8, 4) == 0
+
+
+N = None
+
+
+def test_host_argument_errors_launch_nothing():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(4096)     # never dereferenced: validation fails first
+    # grouped GEMM: N not a multiple of 128 -> UNSUPPORTED_SHAPE
+    assert lib.moe_grouped_gemm_fp8(fake, fake, fake, fake, fake, fake, 2, 256, 100, 256,
+                                    fake, fake, N) == 2
+    # negative rows -> INVALID_ARG
+    assert lib.moe_grouped_gemm_fp8(fake, fake, fake, fake, fake, fake, 2, -1, 128, 256,
+                                    fake, fake, N) == 1
+    # null offsets -> INVALID_ARG
+    assert lib.moe_grouped_gemm_fp8(fake, fake, fake, fake, N, fake, 2, 256, 128, 256,
+                                    fake, fake, N) == 1
+    # misaligned A -> UNSUPPORTED_SHAPE
+    assert lib.moe_grouped_gemm_fp8(ctypes.c_void_p(4097), fake, fake, fake, fake, fake, 2,
+                                    256, 128, 256, fake, fake, N) == 2
+    # act: I not a multiple of 128
+    assert lib.moe_act_requant(fake, fake, fake, 2, 16, 100, fake, fake, fake, N) == 2
+    # combine: K too large / H not a multiple of 128
+    assert lib.moe_combine(fake, 16, fake, fake, 4, 65, 128, fake, fake, N) == 1
+    assert lib.moe_combine(fake, 16, fake, fake, 4, 8, 100, fake, fake, N) == 2
+    # quantize: bad block size, bad dtype flag, rows not a multiple of 128
+    assert lib.moe_quantize_fp8(fake, 0, 128, 128, 2, fake, fake, N) == 1
+    assert lib.moe_quantize_fp8(fake, 2, 128, 128, 1, fake, fake, N) == 1
+    assert lib.moe_quantize_fp8(fake, 0, 100, 128, 128, fake, fake, N) == 2
+    # layout: bad layout enum, E too large, workspace too small, H % 128
+    args = [fake, fake, fake, 16, 2, 4, 256, 5, 128, 512, fake, fake, fake, fake, fake,
+            fake, fake, fake, 1 << 20, fake, N]
+    assert lib.moe_dispatch_layout(*args) == 1
+    a2 = list(args); a2[7] = 0; a2[5] = 2000
+    assert lib.moe_dispatch_layout(*a2) == 1
+    a3 = list(args); a3[7] = 0; a3[18] = 8
+    assert lib.moe_dispatch_layout(*a3) == 1
+    a4 = list(args); a4[7] = 0; a4[6] = 200
+    assert lib.moe_dispatch_layout(*a4) == 2
+    a5 = list(args); a5[7] = 0; a5[8] = 0
+    assert lib.moe_dispatch_layout(*a5) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    import fp8_routed_expert_amd as fre
+    with pytest.raises(ValueError):
+        fre.moe_combine(torch.zeros(4, 128, dtype=torch.bfloat16),
+                        torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2),
+                        torch.zeros(2, 128, dtype=torch.bfloat16),
+                        torch.zeros(1, dtype=torch.int32))
