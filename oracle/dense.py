@@ -60,12 +60,13 @@ def token_forward(x_codes, x_scale, picks, weights, w13d, w2d):
         q = np.empty(I, dtype=np.uint8)
         qs = np.empty(I // 128, dtype=np.float32)
         for b in range(I // 128):
-            blk = act[b * 128:(b + 1) * 128]
+            # codes are decided in fp32: v, amax, s and v / s are fp32 values
+            blk = [np.float32(v) for v in act[b * 128:(b + 1) * 128]]
             amax = max(abs(v) for v in blk)
-            s = np.float32(amax / 448.0) if amax != 0.0 else np.float32(1.0)
+            s = np.float32(amax / np.float32(448.0)) if amax != 0.0 else np.float32(1.0)
             qs[b] = s
             for i, v in enumerate(blk):
-                q[b * 128 + i] = e4m3_encode(np.array([v / float(s)]))[0]
+                q[b * 128 + i] = e4m3_encode(np.array([float(np.float32(v / s))]))[0]
         qv = _dequant_row(q, qs)
         y = np.array([bf16_round(float(np.dot(qv, w2d[e][n]))) for n in range(H)])
         term = float(w) * y

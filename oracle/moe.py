@@ -21,7 +21,9 @@ Readings where the pages are silent (all listed again in the design notes):
   R2  scales are fp32; activations carry one scale per 1x128 block along the
       hidden dimension, weights one per 128x128 block.
   R3  block scale s = fp32(amax / 448); s = 1 when amax = 0; no epsilon floor.
-  R4  codes q = E4M3_RNE(v / s) with saturation to +-448.
+  R4  codes q = E4M3_RNE(v / s) with saturation to +-448; the code is an
+      integer decided by floating point, so v, amax and v / s are taken in
+      fp32 (the device's precision), with correctly rounded division.
   R5  W13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
   R6  activation is SiLU(g) = g * sigmoid(g).
   R7  h, y and out are stored as bf16 (round to nearest even) from exact sums;
@@ -57,19 +59,25 @@ def quantize_blocks(values, block_rows):
     """Quantise a 2-D float array to E4M3 codes with per-block fp32 scales.
 
     Blocks are `block_rows` x 128 (block_rows is 1 for activations, 128 for
-    weights).  For each block: amax = max |v|; s = fp32(amax / 448), or 1 if
-    amax == 0; code = E4M3_RNE(v / s), the quotient taken in fp64 with s as
-    its fp32 value.  Returns (codes uint8 [R, C], scales float32
-    [R / block_rows, C / 128]).
+    weights).  The code of each element is an integer decided by floating
+    point, so it is decided in the precision the device takes it in, fp32
+    (the pages fix none):
+        v    = fp32(value)
+        amax = max |v| over the block
+        s    = fp32(amax / 448), or 1 if amax == 0
+        code = E4M3_RNE(saturate(fp32(v / s)))
+    with IEEE-754 correctly rounded fp32 division.  Returns (codes uint8
+    [R, C], scales float32 [R / block_rows, C / 128]).
     """
-    v = np.asarray(values, dtype=np.float64)
+    v = np.asarray(values).astype(np.float32)
     R, C = v.shape
     assert R % block_rows == 0 and C % BLOCK == 0
     blk = v.reshape(R // block_rows, block_rows, C // BLOCK, BLOCK)
     amax = np.abs(blk).max(axis=(1, 3))
-    s = (amax / E4M3_MAX).astype(np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     s = np.where(amax == 0.0, np.float32(1.0), s).astype(np.float32)
-    q = e4m3_encode(blk / s.astype(np.float64)[:, None, :, None])
+    quot = (blk / s[:, None, :, None]).astype(np.float32)
+    q = e4m3_encode(quot.astype(np.float64))
     return q.reshape(R, C), s
 
 
