@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="source tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first "
+                         "(reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the expert-parallel layer; "
@@ -123,6 +126,12 @@ def main():
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"workload {cfg.name}: E={cfg.E} H={cfg.H} I={cfg.I} T={cfg.T} K={cfg.K}")
     idx, w = routing(cfg)
     R = int((idx >= 0).sum())

@@ -10,34 +10,69 @@
 //                         * sum_{k in kb} a[m, k] * w[e, n, k] )
 //
 // Design (gfx950):
-//   * one workgroup = 256 threads = 4 waves computes a 128x128 tile of c;
-//     each wave owns 64x64 = 4x4 MFMA subtiles of 16x16.
+//   * A workgroup computes a BM x BN = 128 x 128 tile of c with 4 waves; each
+//     wave owns a 64 x 64 sub-tile of 4 x 4 MFMA subtiles of 16 x 16.  Two
+//     workgroups share a CU (64 KB of LDS each), i.e. two waves per SIMD.
 //   * K advances one 128-wide scale block per step.  v_mfma_f32_16x16x128
 //     _f8f6f4 consumes exactly one block per subtile, so each block's raw
-//     fp32 product comes out of a single MFMA (issued with a zero
-//     accumulator) and is promoted into the fp32 accumulator with one FMA by
-//     sa * sw — the scale application the pages put in the epilogue,
-//     applied per block as the block-scaled format requires.
-//   * A and B tiles (128 rows x 128 bytes each) are double-buffered in LDS;
-//     the next block's global loads are in flight while the current block is
-//     multiplied.  16-byte chunks are XOR-swizzled by (row & 7) so that the
-//     fragment reads of 8 consecutive rows hit 8 distinct bank groups.
-//   * tiles are assigned from device-side offsets/counts: m-tiles are
-//     numbered expert by expert (ceil(valid rows / 128) per expert), so the
-//     grid is fixed by the buffer size alone (floor(rows/128) + E m-tiles)
-//     and blocks past the last real tile exit at once.  Nothing is read back
-//     on the host, so the launch can be captured in a hipGraph.
+//     product comes out of a single MFMA issued with a zero accumulator and
+//     is promoted into the fp32 accumulator with one FMA by the combined
+//     scale f = sa[kb, m] * sw[e, nb, kb].  The MFMAs of subtile row i are
+//     issued while the FMAs promote row i - 1, so matrix-core and VALU work
+//     overlap; the accumulators stay in VGPRs.
+//   * A and B tiles (rows x 128 bytes) go from global memory straight into
+//     LDS with buffer_load_dwordx4 ... lds (no staging registers), two
+//     stages deep: the next step's loads are in flight while the current
+//     step is multiplied.  Each stage is its own LDS object and the K loop is
+//     unrolled by two, so the compiler can see that reading one stage never
+//     waits on the loads filling the other; the step barrier orders LDS only
+//     and the tile loads are waited for explicitly.  Inside every 16-row
+//     group the 16-byte chunks are XOR-permuted by ((row >> 1) & 7) -- chosen
+//     through the per-lane global offset, since each load instruction fills
+//     1 KB of LDS contiguously -- so a fragment read (16 rows x 16 bytes per
+//     lane group) touches all 64 banks once.
+//   * Row scales are K-block-major (contiguous per block), prefetched one
+//     step ahead in registers and staged in LDS; the weight-block scale of a
+//     wave's columns is a scalar load.
+//   * Tiles come from device-side offsets/counts: m-tiles are numbered
+//     expert by expert (ceil(valid rows / BM) per expert), so the grid is
+//     fixed by the buffer size alone and workgroups past the last real tile
+//     exit at once; nothing is read back on the host and the launch can be
+//     captured in a hipGraph.  Buffer descriptors bound every tile load, so
+//     rows past the end of the buffer read as zero (and are never stored).
+//   * Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+//     The workgroup id is remapped so that each XCD walks its own contiguous
+//     share of the tile list, which is ordered in groups of GM m-tiles x all
+//     n-tiles (m fastest): the tiles an XCD runs at the same time then share
+//     a few A panels and a few weight panels in that XCD's L2.
 #include "device_common.hpp"
 
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
 constexpr int kBK = 128;
-constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+// Workgroup barrier for the tile pipeline.  __syncthreads() (and even an
+// LDS-scoped fence, since loads into LDS count as vector-memory operations)
+// makes every wave wait for all its outstanding vector loads -- including
+// the tile loads meant to stay in flight across the barrier.  Here the wave
+// waits for its own LDS reads (lgkmcnt) and meets the others; completion of
+// the tile loads is waited for explicitly with wait_vmcnt<n>() before it.
+// Both are compiler memory barriers (asm with a memory clobber), so no
+// memory access is moved across them.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -47,9 +82,16 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
                                                           0, 0);
 }
 
+// Physical position of logical 16-byte chunk c of tile row r: chunks are
+// XOR-permuted by ((r >> 1) & 7), so the 16 rows a fragment read touches at
+// once (16 lanes x 16 bytes) cover all 64 LDS banks exactly once: rows of
+// equal parity sit in the same half of the banks and get 8 distinct chunks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// 32 bytes of row `row` of a swizzled tile: logical 16-byte chunks 2g, 2g+1.
 __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int g) {
   const uint8_t* base = tile + row * kBK;
-  const int sw = row & 7;
+  const int sw = swz(row);
   uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * g) ^ sw) << 4));
   uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * g + 1) ^ sw) << 4));
   v8i r;
@@ -58,160 +100,263 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int g) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
+// Walk the experts' m-tiles (ceil(valid rows / BM) each).  Returns the total
+// number of m-tiles; fills e_sel / row0 / row_end for m-tile `mt` (e_sel = -1
+// if there is no such tile).
+template <int BM>
+__device__ __forceinline__ int find_mtile(const int32_t* offsets, const int32_t* counts,
+                                          int E, int rows_total, int mt, int& e_sel,
+                                          int& row0, int& row_end) {
+  int acc = 0;
+  e_sel = -1;
+  for (int e = 0; e < E; ++e) {
+    int s, en;
+    expert_rows(offsets, counts, e, rows_total, s, en);
+    const int nt = (en - s + BM - 1) / BM;
+    if (e_sel < 0 && mt < acc + nt) {
+      e_sel = e;
+      row0 = s + (mt - acc) * BM;
+      row_end = en;
+    }
+    acc += nt;
+  }
+  return acc;
+}
+
+template <int BM, int BN, int WM, int WN, int GM, int kTag>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
     int E, int rows_total, int N, int K, uint16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * kBK];
-  __shared__ __attribute__((aligned(16))) float sSA[2][kBM];
-  __shared__ float sSB[2];
+  constexpr int NWM = BM / WM;
+  constexpr int NWN = BN / WN;
+  constexpr int NW = NWM * NWN;
+  constexpr int NT = 64 * NW;
+  constexpr int MI = WM / 16;
+  constexpr int NJ = WN / 16;
+  constexpr int NBW = (BN + kBlock - 1) / kBlock;   // weight-scale blocks per tile
+  constexpr int A_CHUNKS = BM / 8;                   // 1 KB LDS chunks per stage
+  constexpr int B_CHUNKS = BN / 8;
+  constexpr int CH_PER_WAVE = (A_CHUNKS + B_CHUNKS) / NW;
+  static_assert((A_CHUNKS + B_CHUNKS) % NW == 0, "chunks must split evenly");
+  static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
+  static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
+  static_assert(BM <= NT, "one thread per tile row for the row scales");
+  static_assert(CH_PER_WAVE % 2 == 0 && A_CHUNKS % 2 == 0, "chunk parity is static");
+  (void)kTag;
 
-  const int n_tiles = N / kBN;
-  const int tile_m = blockIdx.x / n_tiles;
-  const int tile_n = blockIdx.x - tile_m * n_tiles;
+  // one LDS object per stage: the K loop below is unrolled by two so
+  // every access names its stage statically, which lets the compiler see
+  // that reading one stage does not wait on the loads filling another.
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * kBK];
+  // per stage: a_scale of the BM rows
+  __shared__ __attribute__((aligned(16))) float sS0[BM];
+  __shared__ __attribute__((aligned(16))) float sS1[BM];
 
-  // expert and row range of this m-tile
-  int e_sel = -1, row0 = 0, row_end = 0;
-  {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      int s, en;
-      expert_rows(offsets, counts, e, rows_total, s, en);
-      int nt = (en - s + kBM - 1) / kBM;
-      if (tile_m < acc + nt) {
-        e_sel = e;
-        row0 = s + (tile_m - acc) * kBM;
-        row_end = en;
-        break;
-      }
-      acc += nt;
-    }
-  }
+  // ---- which tile: XCD-aware remap, then grouped order over the tile list
+  const int n_tiles = N / BN;
+  int e_sel, row0 = 0, row_end = 0;
+  const int total_m = find_mtile<BM>(offsets, counts, E, rows_total, 0x7fffffff, e_sel,
+                                     row0, row_end);
+  const int total = total_m * n_tiles;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int q = (total + kXcds - 1) / kXcds;   // real tiles per XCD
+  if (slot >= q) return;
+  const int logical = xcd * q + slot;
+  if (logical >= total) return;
+  const int group_size = GM * n_tiles;
+  const int grp = logical / group_size;
+  const int in_grp = logical - grp * group_size;
+  const int gm0 = grp * GM;
+  const int gm_cnt = min(GM, total_m - gm0);
+  const int tile_n = in_grp / gm_cnt;
+  const int tile_m = gm0 + (in_grp - tile_n * gm_cnt);
+  find_mtile<BM>(offsets, counts, E, rows_total, tile_m, e_sel, row0, row_end);
   if (e_sel < 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wm = wave / NWN;
+  const int wn = wave - wm * NWN;
   const int Kb = K / kBK;
   const int nb_w = N / kBlock;
+  const int n0 = tile_n * BN;
 
-  const uint8_t* Wt = W + ((size_t)e_sel * N + (size_t)tile_n * kBN) * K;
-  const float* SWt = SW + ((size_t)e_sel * nb_w + tile_n) * Kb;
+  // ---- direct-to-LDS tile loads through buffer descriptors.  LDS chunk c
+  // (1 KB = 8 rows x 128 B) is filled by one wave instruction: lane p writes
+  // bytes [16p, 16p+16) = row 8c + p/8, physical chunk p%8, which holds the
+  // logical 16-byte chunk (p%8) ^ (p/8) of that row.  The per-lane offset
+  // (row, chunk and K position) is bounds-checked against the descriptor, so
+  // rows past the end of the buffer read as zero and are never stored.
+  // Chunk c holds rows 8c + p/8 with p/8 < 8, so swz() of the row depends on
+  // the parity of c only: one lane offset per parity.
+  const uint32_t lane_row = (uint32_t)(lane >> 3) * (uint32_t)K;
+  const uint32_t lane_off0 = lane_row + (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4);
+  const uint32_t lane_off1 = lane_row + (uint32_t)(((lane & 7) ^ swz(8 + (lane >> 3))) << 4);
+  const long long a_bytes = (long long)(rows_total - row0) * K;
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (size_t)row0 * K), (short)0,
+      (int)(a_bytes > 0x7ffff000LL ? 0x7ffff000LL : a_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + ((size_t)e_sel * N + n0) * K), (short)0, BN * K, 0x00020000);
 
-  const int ld_row = tid >> 3;
-  const int ld_ch = tid & 7;
-  // global->LDS staging: thread tid moves 16-byte chunk (tid & 7) of rows
-  // (tid >> 3) + 32 i, i < 4, of both tiles (explicit registers, no arrays,
-  // so nothing is placed in scratch memory)
-#define MOE_ROW_PTRS(i)                                                        \
-  const uint8_t* a_src##i;                                                     \
-  const uint8_t* b_src##i;                                                     \
-  {                                                                            \
-    int r = row0 + ld_row + 32 * i;                                            \
-    r = r < rows_total ? r : rows_total - 1;                                   \
-    a_src##i = A + (size_t)r * K + ld_ch * 16;                                 \
-    b_src##i = Wt + (size_t)(ld_row + 32 * i) * K + ld_ch * 16;                \
-  }
-  MOE_ROW_PTRS(0)
-  MOE_ROW_PTRS(1)
-  MOE_ROW_PTRS(2)
-  MOE_ROW_PTRS(3)
-#undef MOE_ROW_PTRS
-  int sa_row = row0 + (tid & (kBM - 1));
+  // Row scales (K-block-major, so a tile's rows are contiguous) are loaded
+  // into registers one step ahead by the first BM threads and written to the
+  // stage's scale block at the end of the step; rows past the buffer are
+  // clamped and only feed rows that are never stored.  The weight-block
+  // scale of this wave's columns is one wave-uniform value per step, read
+  // with a scalar load one step ahead.
+  const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * Kb;
+  const bool row_owner = tid < BM;
+  int sa_row = row0 + (row_owner ? tid : 0);
   sa_row = sa_row < rows_total ? sa_row : rows_total - 1;
 
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-  float rsa = 0.f, rsb = 0.f;
-#define MOE_GLOAD(kb)                                                          \
-  do {                                                                         \
-    const size_t ko = (size_t)(kb) * kBK;                                      \
-    ra0 = *reinterpret_cast<const uint4*>(a_src0 + ko);                        \
-    ra1 = *reinterpret_cast<const uint4*>(a_src1 + ko);                        \
-    ra2 = *reinterpret_cast<const uint4*>(a_src2 + ko);                        \
-    ra3 = *reinterpret_cast<const uint4*>(a_src3 + ko);                        \
-    rb0 = *reinterpret_cast<const uint4*>(b_src0 + ko);                        \
-    rb1 = *reinterpret_cast<const uint4*>(b_src1 + ko);                        \
-    rb2 = *reinterpret_cast<const uint4*>(b_src2 + ko);                        \
-    rb3 = *reinterpret_cast<const uint4*>(b_src3 + ko);                        \
-    if (tid < kBM) rsa = SA[(size_t)(kb) * rows_total + sa_row];               \
-    if (tid == kBM) rsb = SWt[(kb)];                                           \
-  } while (0)
-#define MOE_ST1(buf, i)                                                        \
-  {                                                                            \
-    const int row = ld_row + 32 * i;                                           \
-    const int off = row * kBK + ((ld_ch ^ (row & 7)) << 4);                    \
-    *reinterpret_cast<uint4*>(&sA[(buf)][off]) = ra##i;                        \
-    *reinterpret_cast<uint4*>(&sB[(buf)][off]) = rb##i;                        \
-  }
-#define MOE_SSTORE(buf)                                                        \
-  do {                                                                         \
-    MOE_ST1(buf, 0) MOE_ST1(buf, 1) MOE_ST1(buf, 2) MOE_ST1(buf, 3)            \
-    if (tid < kBM) sSA[(buf)][tid] = rsa;                                      \
-    if (tid == kBM) sSB[(buf)] = rsb;                                          \
-  } while (0)
-
-  v4f acc[4][4];
+  // Every wave issues the same CH_PER_WAVE tile-chunk loads per stage.
+  auto issue = [&](int kb, uint8_t* stA, uint8_t* stB) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < CH_PER_WAVE; ++u) {
+      const int c = wave * CH_PER_WAVE + u;   // wave-uniform
+      const uint32_t kofs = (uint32_t)kb * kBK;
+      const uint32_t lo = (u & 1) ? lane_off1 : lane_off0;   // parity of c is u's
+      if (c < A_CHUNKS) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc_a, (lds_void*)(stA + c * 1024), 16,
+            (int)(lo + (uint32_t)(c * 8) * (uint32_t)K + kofs), 0, 0, 0);
+      } else {
+        const int cb = c - A_CHUNKS;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc_b, (lds_void*)(stB + cb * 1024), 16,
+            (int)(lo + (uint32_t)(cb * 8) * (uint32_t)K + kofs), 0, 0, 0);
+      }
+    }
+  };
 
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
-  __syncthreads();
+  v4f acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  for (int kb = 0; kb < Kb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < Kb) MOE_GLOAD(kb + 1);
-    v8i af[4], bf[4];
+  const int wcol = wn * WN;
+  float sw_cur = 0.f;   // weight-block scale of the current step
+
+  // One K step on stage (tA, tB, tS).  The B fragments are read first, then
+  // the loads of step kb + 1 are issued into the other stage (freed by the
+  // barrier ending the previous step) and stay in flight while the step's
+  // MFMAs run; the A fragments and row scales are read row by row as the
+  // MFMA pipeline needs them.
+  auto step = [&](int kb, const uint8_t* tA, const uint8_t* tB, const float* tS, uint8_t* nA,
+                  uint8_t* nB, float* nS) {
+    v8i bf[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = load_frag(sA[cur], wm * 64 + i * 16 + r16, g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = load_frag(sB[cur], wn * 64 + j * 16 + r16, g);
-    const float sb = sSB[cur];
-    float f[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 s4 = *reinterpret_cast<const float4*>(&sSA[cur][wm * 64 + i * 16 + 4 * g]);
-      f[i][0] = s4.x * sb;
-      f[i][1] = s4.y * sb;
-      f[i][2] = s4.z * sb;
-      f[i][3] = s4.w * sb;
+    for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
+    float sa_next = 0.f;
+    if (kb + 1 < Kb) {
+      issue(kb + 1, nA, nB);
+      if (row_owner) sa_next = SA[(size_t)(kb + 1) * rows_total + sa_row];
     }
+    const float sw = sw_cur;
+    sw_cur = kb + 1 < Kb ? SWw[kb + 1] : 0.f;
+    // two-deep software pipeline over the wave's MFMA rows: the MFMAs of
+    // row i are issued while the FMAs promote row i-1 (whose products are
+    // complete), so matrix-core and VALU work overlap and only two sets of
+    // raw products are live.
+    v4f tprev[NJ];
+    float4 fprev = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i <= MI; ++i) {
+      v4f tcur[NJ];
+      float4 fcur = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < MI) {
+        const v8i af = load_frag(tA, wm * WM + i * 16 + r16, g);
+        const float4 fs = *reinterpret_cast<const float4*>(&tS[wm * WM + i * 16 + 4 * g]);
+        fcur = make_float4(fs.x * sw, fs.y * sw, fs.z * sw, fs.w * sw);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v4f t = mfma_fp8_16x16x128(af[i], bf[j]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(t[r], f[i][r], acc[i][j][r]);
+        for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(af, bf[j]);
       }
-    if (kb + 1 < Kb) MOE_SSTORE(cur ^ 1);
-    __syncthreads();
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i - 1][j][0] = fmaf(tprev[j][0], fprev.x, acc[i - 1][j][0]);
+          acc[i - 1][j][1] = fmaf(tprev[j][1], fprev.y, acc[i - 1][j][1]);
+          acc[i - 1][j][2] = fmaf(tprev[j][2], fprev.z, acc[i - 1][j][2]);
+          acc[i - 1][j][3] = fmaf(tprev[j][3], fprev.w, acc[i - 1][j][3]);
+        }
+      }
+      if (i < MI) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
+        fprev = fcur;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // keep the promotions of this step ahead of the barrier (otherwise they
+    // are sunk into the next step, where they no longer overlap the MFMAs)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
+    if (kb + 1 < Kb && row_owner) nS[tid] = sa_next;
+    // the next stage must have landed for every wave before it is read
+    wait_vmcnt<0>();
+    lds_barrier();
+  };
+
+  sw_cur = SWw[0];
+  issue(0, sA0, sB0);
+  if (row_owner) sS0[tid] = SA[sa_row];
+  wait_vmcnt<0>();
+  lds_barrier();
+  for (int kb = 0; kb < Kb; kb += 2) {
+    step(kb, sA0, sB0, sS0, sA1, sB1, sS1);
+    if (kb + 1 < Kb) step(kb + 1, sA1, sB1, sS1, sA0, sB0, sS0);
   }
 
-  // epilogue: lane holds rows 4g..4g+3 of each 16x16 subtile, column r16
+  // ---- epilogue: lane holds rows 4g..4g+3 of each 16x16 subtile, column r16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int row = row0 + wm * 64 + i * 16 + 4 * g + r;
+      const int row = row0 + wm * WM + i * 16 + 4 * g + r;
       if (row < row_end) {
-        uint16_t* crow = C + (size_t)row * N + (size_t)tile_n * kBN + wn * 64 + r16;
+        uint16_t* crow = C + (size_t)row * N + n0 + wcol + r16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) crow[j * 16] = f32_to_bf16(acc[i][j][r]);
+        for (int j = 0; j < NJ; ++j) crow[j * 16] = f32_to_bf16(acc[i][j][r]);
       }
     }
-#undef MOE_GLOAD
-#undef MOE_ST1
-#undef MOE_SSTORE
 }
+
+template <int BM, int BN, int WM, int WN, int GM, int kTag>
+static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
+                           const float* w_scale, const int32_t* offsets,
+                           const int32_t* counts, int E, int rows_total, int N, int K,
+                           uint16_t* c, hipStream_t st) {
+  if (N % BN != 0) return MOE_UNSUPPORTED_SHAPE;
+  long long m_tiles = (long long)rows_total / BM + E;
+  long long blocks = m_tiles * (N / BN);
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
+  constexpr int threads = 64 * (BM / WM) * (BN / WN);
+  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag>),
+                     dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
+                     offsets, counts, E, rows_total, N, K, c);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}
+
+// Tile configuration (BM, BN, WM, WN, GM).  kTag keeps the gate/up (1) and
+// down (2) projections as separate kernel symbols so that profiles attribute
+// time per projection.
+#ifndef MOE_GEMM_CFG
+#define MOE_GEMM_CFG 128, 128, 64, 64, 4
+#endif
 
 }  // namespace moe
 
@@ -225,18 +370,15 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(
   (void)status_dev;
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || N <= 0 || K <= 0)
     return MOE_INVALID_ARG;
-  if (N % kBN != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
+  if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts || !w || !w_scale) return MOE_INVALID_ARG;
   if (rows_total == 0) return MOE_OK;
   if (!a || !a_scale || !c) return MOE_INVALID_ARG;
-  if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15)
-    return MOE_UNSUPPORTED_SHAPE;
-  long long m_tiles = (long long)rows_total / kBM + E;
-  long long blocks = m_tiles * (N / kBN);
-  if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
+  if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(grouped_gemm_fp8_kernel, dim3((unsigned)blocks),
-                     dim3(kThreads), 0, st, a, a_scale, w, w_scale, offsets,
-                     counts, E, rows_total, N, K, c);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+  const bool gate_up = K > N;   // gate/up: K = H > N = 2I; down: N = H > K = I
+  return gate_up ? launch<MOE_GEMM_CFG, 1>(a, a_scale, w, w_scale, offsets, counts, E,
+                                           rows_total, N, K, c, st)
+                 : launch<MOE_GEMM_CFG, 2>(a, a_scale, w, w_scale, offsets, counts, E,
+                                           rows_total, N, K, c, st);
 }

@@ -146,7 +146,9 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, const uint8_t* x,
  *   w        [E, N, K] e4m3            w_scale [E, N/128, K/128] f32
  *   offsets  [E+1], counts [E] int32 on the device (from moe_dispatch_layout)
  *   c        [rows_total, N] bf16; only valid rows are written
- * Segments outside the buffer are clipped and set MOE_ERR_BAD_INDEX.
+ * Segments reaching outside the buffer are clipped to it (rows the layout
+ * call dropped are reported there, with MOE_ERR_OVERFLOW); status_dev is
+ * accepted for uniformity and not written.
  */
 moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
                                   const uint8_t* w, const float* w_scale,
@@ -165,6 +167,7 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
  *
  *   h        [rows_total, 2I] bf16
  *   q        [rows_total, I] e4m3     q_scale [I/128, rows_total] f32
+ * status_dev is accepted for uniformity and not written.
  */
 moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
                              const int32_t* counts, int E, int rows_total,

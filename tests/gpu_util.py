@@ -38,7 +38,7 @@ def bf16_vals(t):
     return bf16_decode(host(t))
 
 
-def check_close(got, ref, what):
+def check_close(got, ref, what, rel_l2_tol=REL_L2_TOL):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -49,7 +49,7 @@ def check_close(got, ref, what):
     maxerr = np.abs(d).max() if d.size else 0.0
     bound = MAX_ERR_FRAC * (np.abs(ref).max() if ref.size else 0.0)
     log(f"{what}: rel_l2={rel:.3e} max_err={maxerr:.3e} bound={bound:.3e} n={ref.size}")
-    assert rel <= REL_L2_TOL, f"{what}: relative L2 {rel:.3e} > {REL_L2_TOL}"
+    assert rel <= rel_l2_tol, f"{what}: relative L2 {rel:.3e} > {rel_l2_tol}"
     assert maxerr <= bound, f"{what}: max |err| {maxerr:.3e} > {bound:.3e}"
     return rel
 
