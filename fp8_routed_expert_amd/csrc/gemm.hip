@@ -143,6 +143,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
   static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
   static_assert(BM <= NT, "one thread per tile row for the row scales");
+  static_assert(MI % 4 == 0, "row scales are read four at a time");
   static_assert(CH_PER_WAVE % 2 == 0 && A_CHUNKS % 2 == 0, "chunk parity is static");
   (void)kTag;
 
@@ -209,13 +210,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // Row scales (K-block-major, so a tile's rows are contiguous) are loaded
   // into registers one step ahead by the first BM threads and written to the
   // stage's scale block at the end of the step; rows past the buffer are
-  // clamped and only feed rows that are never stored.  The weight-block
-  // scale of this wave's columns is one wave-uniform value per step, read
-  // with a scalar load one step ahead.
+  // clamped and only feed rows that are never stored.  In LDS row
+  // wm*WM + i*16 + q sits at ((wm*16 + q) * MI + i), so a lane -- whose
+  // outputs all belong to row q of each of its MI subtiles -- reads its MI
+  // scales as one contiguous run.  The weight-block scale of this wave's
+  // columns is one wave-uniform value per step, read with a scalar load one
+  // step ahead.
   const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * Kb;
   const bool row_owner = tid < BM;
   int sa_row = row0 + (row_owner ? tid : 0);
   sa_row = sa_row < rows_total ? sa_row : rows_total - 1;
+  const int sa_pos = ((tid / WM) * 16 + (tid & 15)) * MI + (tid % WM) / 16;
 
   // Every wave issues the same CH_PER_WAVE tile-chunk loads per stage.
   auto issue = [&](int kb, uint8_t* stA, uint8_t* stB) {
@@ -248,16 +253,25 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int wcol = wn * WN;
   float sw_cur = 0.f;   // weight-block scale of the current step
 
-  // One K step on stage (tA, tB, tS).  The B fragments are read first, then
-  // the loads of step kb + 1 are issued into the other stage (freed by the
-  // barrier ending the previous step) and stay in flight while the step's
-  // MFMAs run; the A fragments and row scales are read row by row as the
+  // One K step on stage (tA, tB, tS).  The MFMAs compute the transposed
+  // product (weights as the first operand), so a lane's four outputs of a
+  // subtile are four consecutive columns of one row: one row scale per
+  // lane and subtile.  The B fragments and the lane's row scales are read
+  // first, then the loads of step kb + 1 are issued into the other stage
+  // (freed by the barrier ending the previous step) and stay in flight
+  // while the step's MFMAs run; the A fragments are read row by row as the
   // MFMA pipeline needs them.
   auto step = [&](int kb, const uint8_t* tA, const uint8_t* tB, const float* tS, uint8_t* nA,
                   uint8_t* nB, float* nS) {
     v8i bf[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
+    float fs[MI];
+#pragma unroll
+    for (int i4 = 0; i4 < MI; i4 += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(&tS[(wm * 16 + r16) * MI + i4]);
+      fs[i4] = v.x; fs[i4 + 1] = v.y; fs[i4 + 2] = v.z; fs[i4 + 3] = v.w;
+    }
     float sa_next = 0.f;
     if (kb + 1 < Kb) {
       issue(kb + 1, nA, nB);
@@ -269,26 +283,28 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     // row i are issued while the FMAs promote row i-1 (whose products are
     // complete), so matrix-core and VALU work overlap and only two sets of
     // raw products are live.
+    // The A fragment of row i + 1 is read while row i is multiplied.
     v4f tprev[NJ];
-    float4 fprev = make_float4(0.f, 0.f, 0.f, 0.f);
+    float fprev = 0.f;
+    v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
     for (int i = 0; i <= MI; ++i) {
       v4f tcur[NJ];
-      float4 fcur = make_float4(0.f, 0.f, 0.f, 0.f);
+      float fcur = 0.f;
       if (i < MI) {
-        const v8i af = load_frag(tA, wm * WM + i * 16 + r16, g);
-        const float4 fs = *reinterpret_cast<const float4*>(&tS[wm * WM + i * 16 + 4 * g]);
-        fcur = make_float4(fs.x * sw, fs.y * sw, fs.z * sw, fs.w * sw);
+        const v8i af = af_next;
+        if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
+        fcur = fs[i] * sw;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(af, bf[j]);
+        for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(bf[j], af);
       }
       if (i > 0) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          acc[i - 1][j][0] = fmaf(tprev[j][0], fprev.x, acc[i - 1][j][0]);
-          acc[i - 1][j][1] = fmaf(tprev[j][1], fprev.y, acc[i - 1][j][1]);
-          acc[i - 1][j][2] = fmaf(tprev[j][2], fprev.z, acc[i - 1][j][2]);
-          acc[i - 1][j][3] = fmaf(tprev[j][3], fprev.w, acc[i - 1][j][3]);
+          acc[i - 1][j][0] = fmaf(tprev[j][0], fprev, acc[i - 1][j][0]);
+          acc[i - 1][j][1] = fmaf(tprev[j][1], fprev, acc[i - 1][j][1]);
+          acc[i - 1][j][2] = fmaf(tprev[j][2], fprev, acc[i - 1][j][2]);
+          acc[i - 1][j][3] = fmaf(tprev[j][3], fprev, acc[i - 1][j][3]);
         }
       }
       if (i < MI) {
@@ -304,7 +320,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
-    if (kb + 1 < Kb && row_owner) nS[tid] = sa_next;
+    if (kb + 1 < Kb && row_owner) nS[sa_pos] = sa_next;
     // the next stage must have landed for every wave before it is read
     wait_vmcnt<0>();
     lds_barrier();
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 
   sw_cur = SWw[0];
   issue(0, sA0, sB0);
-  if (row_owner) sS0[tid] = SA[sa_row];
+  if (row_owner) sS0[sa_pos] = SA[sa_row];
   wait_vmcnt<0>();
   lds_barrier();
   for (int kb = 0; kb < Kb; kb += 2) {
@@ -320,18 +336,22 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     if (kb + 1 < Kb) step(kb + 1, sA1, sB1, sS1, sA0, sB0, sS0);
   }
 
-  // ---- epilogue: lane holds rows 4g..4g+3 of each 16x16 subtile, column r16
+  // ---- epilogue: in subtile (i, j) a lane holds row r16 and columns
+  // 4g .. 4g+3: four bf16 values, one 8-byte store
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i) {
+    const int row = row0 + wm * WM + i * 16 + r16;
+    if (row < row_end) {
+      uint16_t* crow = C + (size_t)row * N + n0 + wcol + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + wm * WM + i * 16 + 4 * g + r;
-      if (row < row_end) {
-        uint16_t* crow = C + (size_t)row * N + n0 + wcol + r16;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) crow[j * 16] = f32_to_bf16(acc[i][j][r]);
+      for (int j = 0; j < NJ; ++j) {
+        uint2 o;
+        o.x = f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+        o.y = f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(crow + j * 16) = o;
       }
     }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int GM, int kTag>
@@ -351,11 +371,16 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
-// Tile configuration (BM, BN, WM, WN, GM).  kTag keeps the gate/up (1) and
-// down (2) projections as separate kernel symbols so that profiles attribute
-// time per projection.
-#ifndef MOE_GEMM_CFG
-#define MOE_GEMM_CFG 128, 128, 64, 64, 4
+// Tile configurations (BM, BN, WM, WN, GM).  Large problems use 256 x 256
+// tiles (8 waves of 128 x 64, two per SIMD); problems too small to give
+// every CU two such tiles use 128 x 128 (4 waves of 64 x 64, two workgroups
+// per CU).  kTag keeps the gate/up (1) and down (2) projections as separate
+// kernel symbols so that profiles attribute time per projection.
+#ifndef MOE_GEMM_BIG
+#define MOE_GEMM_BIG 256, 256, 128, 64, 4
+#endif
+#ifndef MOE_GEMM_SMALL
+#define MOE_GEMM_SMALL 128, 128, 64, 64, 4
 #endif
 
 }  // namespace moe
@@ -377,8 +402,15 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(
   if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool gate_up = K > N;   // gate/up: K = H > N = 2I; down: N = H > K = I
-  return gate_up ? launch<MOE_GEMM_CFG, 1>(a, a_scale, w, w_scale, offsets, counts, E,
-                                           rows_total, N, K, c, st)
-                 : launch<MOE_GEMM_CFG, 2>(a, a_scale, w, w_scale, offsets, counts, E,
-                                           rows_total, N, K, c, st);
+  // host-known sizes only, so the choice is the same inside graph capture
+  const bool big = N % 256 == 0 && (long long)(rows_total / 256) * (N / 256) >= 512;
+  if (big)
+    return gate_up ? launch<MOE_GEMM_BIG, 1>(a, a_scale, w, w_scale, offsets, counts, E,
+                                             rows_total, N, K, c, st)
+                   : launch<MOE_GEMM_BIG, 2>(a, a_scale, w, w_scale, offsets, counts, E,
+                                             rows_total, N, K, c, st);
+  return gate_up ? launch<MOE_GEMM_SMALL, 1>(a, a_scale, w, w_scale, offsets, counts, E,
+                                             rows_total, N, K, c, st)
+                 : launch<MOE_GEMM_SMALL, 2>(a, a_scale, w, w_scale, offsets, counts, E,
+                                             rows_total, N, K, c, st);
 }
