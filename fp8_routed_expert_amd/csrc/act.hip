@@ -4,18 +4,51 @@
 // GB200 NVL72 with PD and Large Scale EP (Part I)", section 方法实现细节) but
 // not the activation; SiLU-gated FFN with gate rows first is the reading.
 //
-// One workgroup per permuted row; each lane holds 8 consecutive columns, so
-// 16 lanes hold one 128-wide scale block and the block amax is a 4-step
-// butterfly inside the 16-lane group.  Reads 4 bytes and writes 1 byte per
-// element: bound by HBM bandwidth.
+// A flat grid: workgroup (m, y) holds columns [2048 y, 2048 y + 2048) of
+// permuted row m, 8 consecutive columns per lane, so 16 lanes hold one
+// 128-wide scale block and the block amax is a 4-step butterfly inside the
+// 16-lane group.  The gate and up loads are issued first; the check that m
+// is a valid row (a short search over the segment starts) runs while they
+// are in flight, and only the stores depend on it.  Reads 4 bytes and writes
+// ~1 byte per element: bound by HBM bandwidth.
 #include "device_common.hpp"
 
 namespace moe {
 
 constexpr int kActThreads = 256;
+constexpr int kActCols = kActThreads * 8;   // columns per workgroup
 
+// silu(g) * u in fp32: exp(-g) as the hardware base-2 exponential of
+// -g log2(e), and the hardware reciprocal (each good to about 1 ulp).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// v / s correctly rounded, from y = RN(1/s): q0 = RN(v y) is within an ulp,
+// the residual v - s q0 is then exact in one fma, and q0 + residual * y
+// rounds to the correctly rounded quotient (Markstein's division theorem).
+// Exactness of the residual needs its bits above the fp32 underflow range;
+// for s >= 2^-90 that holds whenever |v / s| >= 2^-11, and smaller quotients
+// encode to zero in E4M3 either way.  Smaller scales take a real division.
+__device__ __forceinline__ float div_scale(float v, float s, float y) {
+  const float q0 = v * y;
+  const float r = fmaf(-s, q0, v);
+  return fmaf(r, y, q0);
+}
+
+// Is permuted row m inside an expert segment?  Binary search for the last
+// segment start <= m, then check that segment's valid range.
+__device__ __forceinline__ bool row_valid(const int32_t* offsets, const int32_t* counts,
+                                          int E, int rows_total, int m) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  int s, en;
+  expert_rows(offsets, counts, lo, rows_total, s, en);
+  return m >= s && m < en;
 }
 
 __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
@@ -23,39 +56,42 @@ __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
     const int32_t* __restrict__ counts, int E, int rows_total, int I,
     uint8_t* __restrict__ q, float* __restrict__ q_scale) {
   const int m = blockIdx.x;
-  // is m a valid row?  binary search for the last segment start <= m
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (offsets[mid] <= m) lo = mid; else hi = mid - 1;
-  }
-  int s, en;
-  expert_rows(offsets, counts, lo, rows_total, s, en);
-  if (m < s || m >= en) return;
-
+  const int j0 = blockIdx.y * kActCols + threadIdx.x * 8;
+  const bool in_row = j0 < I;
   const uint16_t* hrow = h + (size_t)m * 2 * I;
-  uint8_t* qrow = q + (size_t)m * I;
-  for (int j0 = threadIdx.x * 8; j0 < I; j0 += kActThreads * 8) {
-    uint4 gv = *reinterpret_cast<const uint4*>(hrow + j0);
-    uint4 uv = *reinterpret_cast<const uint4*>(hrow + I + j0);
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
-    float v[8];
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = silu_mul(bf16_to_f32(gw[i] & 0xffffu), bf16_to_f32(uw[i] & 0xffffu));
-      v[2 * i + 1] = silu_mul(bf16_to_f32(gw[i] >> 16), bf16_to_f32(uw[i] >> 16));
-      amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
-    }
-    amax = group16_max(amax);
-    const float sc = block_scale(amax);
-    uint2 out;
-    out.x = pack2_e4m3(v[0] / sc, v[1] / sc) | (pack2_e4m3(v[2] / sc, v[3] / sc) << 16);
-    out.y = pack2_e4m3(v[4] / sc, v[5] / sc) | (pack2_e4m3(v[6] / sc, v[7] / sc) << 16);
-    *reinterpret_cast<uint2*>(qrow + j0) = out;
-    if ((threadIdx.x & 15) == 0) q_scale[(size_t)(j0 / kBlock) * rows_total + m] = sc;
+  uint4 gv = make_uint4(0, 0, 0, 0), uv = gv;
+  if (in_row) {
+    gv = *reinterpret_cast<const uint4*>(hrow + j0);
+    uv = *reinterpret_cast<const uint4*>(hrow + I + j0);
   }
+  if (!row_valid(offsets, counts, E, rows_total, m)) return;   // uniform
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  float v[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = silu_mul(bf16_to_f32(gw[i] & 0xffffu), bf16_to_f32(uw[i] & 0xffffu));
+    v[2 * i + 1] = silu_mul(bf16_to_f32(gw[i] >> 16), bf16_to_f32(uw[i] >> 16));
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  amax = group16_max(amax);   // all 16 lanes of a block share in_row
+  if (!in_row) return;
+  const float sc = block_scale(amax);
+  float qv[8];
+  if (sc >= 0x1p-90f) {
+    const float y = 1.0f / sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = div_scale(v[i], sc, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = v[i] / sc;
+  }
+  uint2 out;
+  out.x = pack2_e4m3(qv[0], qv[1]) | (pack2_e4m3(qv[2], qv[3]) << 16);
+  out.y = pack2_e4m3(qv[4], qv[5]) | (pack2_e4m3(qv[6], qv[7]) << 16);
+  *reinterpret_cast<uint2*>(q + (size_t)m * I + j0) = out;
+  if ((threadIdx.x & 15) == 0) q_scale[(size_t)(j0 / kBlock) * rows_total + m] = sc;
 }
 
 }  // namespace moe
@@ -63,10 +99,9 @@ __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
 using namespace moe;
 
 extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
-                                        const int32_t* counts, int E,
-                                        int rows_total, int I, uint8_t* q,
-                                        float* q_scale, int32_t* status_dev,
-                                        void* stream) {
+                                        const int32_t* counts, int E, int rows_total,
+                                        int I, uint8_t* q, float* q_scale,
+                                        int32_t* status_dev, void* stream) {
   (void)status_dev;
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0) return MOE_INVALID_ARG;
   if (I % kBlock != 0) return MOE_UNSUPPORTED_SHAPE;
@@ -75,7 +110,9 @@ extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offset
   if (!h || !q || !q_scale) return MOE_INVALID_ARG;
   if (((uintptr_t)h | (uintptr_t)q) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(act_requant_kernel, dim3((unsigned)rows_total), dim3(kActThreads),
-                     0, st, h, offsets, counts, E, rows_total, I, q, q_scale);
+  hipLaunchKernelGGL(act_requant_kernel,
+                     dim3((unsigned)rows_total, (unsigned)((I + kActCols - 1) / kActCols)),
+                     dim3(kActThreads), 0, st, h, offsets, counts, E, rows_total, I, q,
+                     q_scale);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }

@@ -40,13 +40,22 @@ __device__ __forceinline__ uint32_t pack2_e4m3(float a, float b) {
          0xffffu;
 }
 
-// Reductions over aligned groups of 16 lanes (one 128-wide block held as
-// 8 values per lane).
+// Lane permutation inside rows of 16 lanes (DPP control word kCtrl).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Maximum over an aligned group of 16 lanes (one 128-wide block held as 8
+// values per lane), left in every lane of the group.  Lanes are swapped in
+// pairs, then pairs of pairs (quad permutations 1032 and 2301), then each
+// 8-lane half is mirrored onto itself and the 16-lane row onto itself, so
+// every lane has met all 16 values.  All 16 lanes must be active.
 __device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, dpp_row<0xb1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_row<0x4e>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_row<0x140>(v));   // row_mirror
   return v;
 }
 

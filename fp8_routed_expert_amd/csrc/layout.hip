@@ -16,6 +16,8 @@
 //                  writes slot_of, row_src, row_expert
 //   permute_rows   one wave per source token: reads x[t] once, writes it to
 //                  each of the token's slots (16-byte accesses)
+//   permute_scales the matching scales, 64 slots per workgroup transposed
+//                  through LDS (contiguous reads and stores)
 #include "device_common.hpp"
 
 namespace moe {
@@ -172,51 +174,76 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank(
 }
 
 // One wave per source token: the token's row is read from HBM once (16-byte
-// loads, 64 lanes side by side) and written to every slot it was given.
-// Scales go to the K-block-major a_scale layout.
+// loads, 64 lanes side by side, all of a row's loads in flight together)
+// and written to every slot it was given.
+constexpr int kPermChunks = 8;   // 16-byte chunks per lane per pass (H <= 8192 in one pass)
+
 __global__ __launch_bounds__(256) void permute_rows(
-    const uint8_t* __restrict__ x, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ slot_of, int T, int K, int H,
-    int rows_total, uint8_t* __restrict__ a, float* __restrict__ a_scale) {
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ slot_of, int T, int K, int H,
+    int rows_total, uint8_t* __restrict__ a) {
   const int lane = threadIdx.x & 63;
   const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int s = lane < K ? slot_of[t * K + lane] : -1;
-  unsigned long long vm = __ballot(s >= 0 && s < rows_total);
-  if (vm == 0) return;
+  // the token's slots and its first chunks are requested together; only the
+  // stores wait for the slots
+  const int s = lane < K ? slot_of[t * K + lane] : -1;
   const int n16 = H >> 4;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
-  constexpr int kUnroll = 4;
-  for (int c0 = lane; c0 < n16; c0 += 64 * kUnroll) {
-    uint4 v[kUnroll];
+  for (int c0 = lane; c0 < n16; c0 += 64 * kPermChunks) {
+    uint4 v[kPermChunks];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int c = c0 + u * 64;
-      if (c < n16) v[u] = src[c];
+    for (int u = 0; u < kPermChunks; ++u) {
+      const int c = c0 + u * 64;
+      v[u] = src[c < n16 ? c : 0];   // past the row: re-read chunk 0, not stored
     }
-    unsigned long long m = vm;
+    unsigned long long m = __ballot(s >= 0 && s < rows_total);
     while (m) {
-      int k = __ffsll((long long)m) - 1;
+      const int k = __ffsll((long long)m) - 1;
       m &= m - 1;
-      int slot = __builtin_amdgcn_readlane(s, k);
+      const int slot = __builtin_amdgcn_readlane(s, k);
       uint4* dst = reinterpret_cast<uint4*>(a + (long long)slot * H);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        int c = c0 + u * 64;
+      for (int u = 0; u < kPermChunks; ++u) {
+        const int c = c0 + u * 64;
         if (c < n16) dst[c] = v[u];
       }
     }
   }
-  const int hb = H / kBlock;
-  for (int kb = lane; kb < hb; kb += 64) {
-    float sc = x_scale[t * hb + kb];
-    unsigned long long m = vm;
-    while (m) {
-      int k = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      int slot = __builtin_amdgcn_readlane(s, k);
-      a_scale[(long long)kb * rows_total + slot] = sc;
+}
+
+// Scales in the permuted, K-block-major layout: a_scale[kb, slot] =
+// x_scale[row_src[slot], kb].  A workgroup takes 64 consecutive slots and
+// transposes through LDS: each wave reads whole source scale rows (64
+// consecutive block scales of one token) and writes 64 consecutive slots of
+// one block column, so both sides are contiguous runs.
+constexpr int kScTile = 64;
+
+__global__ __launch_bounds__(256) void permute_scales(
+    const float* __restrict__ x_scale, const int32_t* __restrict__ row_src, int T, int hb,
+    int rows_total, float* __restrict__ a_scale) {
+  __shared__ float tile[64][kScTile + 1];
+  __shared__ int src_of[kScTile];
+  const int slot0 = blockIdx.x * kScTile;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x < kScTile) {
+    const int slot = slot0 + threadIdx.x;
+    const int src = slot < rows_total ? row_src[slot] : -1;
+    src_of[threadIdx.x] = (src >= 0 && src < T) ? src : -1;
+  }
+  __syncthreads();
+  for (int kb0 = 0; kb0 < hb; kb0 += 64) {
+    const int kb = kb0 + lane;
+#pragma unroll
+    for (int r = 0; r < kScTile; r += 4) {
+      const int src = src_of[r + wv];
+      if (src >= 0 && kb < hb) tile[lane][r + wv] = x_scale[(long long)src * hb + kb];
     }
+    __syncthreads();
+    const bool live = src_of[lane] >= 0;
+    const long long slot = slot0 + lane;
+    for (int c = wv; c < 64 && kb0 + c < hb; c += 4)
+      if (live) a_scale[(long long)(kb0 + c) * rows_total + slot] = tile[c][lane];
+    __syncthreads();
   }
 }
 
@@ -293,9 +320,12 @@ extern "C" moe_status_t moe_dispatch_layout(
                        E, key_bits_for(E), layout, (int)rows_total, cap,
                        offsets, chunk_base, slot_of, row_src, row_expert,
                        status_dev);
-  if (T > 0 && rows_total > 0)
-    hipLaunchKernelGGL(permute_rows, dim3((unsigned)((T + 3) / 4)), dim3(256),
-                       0, st, x, x_scale, slot_of, T, K, H, (int)rows_total, a,
+  if (T > 0 && rows_total > 0) {
+    hipLaunchKernelGGL(permute_rows, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x,
+                       slot_of, T, K, H, (int)rows_total, a);
+    hipLaunchKernelGGL(permute_scales, dim3((unsigned)((rows_total + kScTile - 1) / kScTile)),
+                       dim3(256), 0, st, x_scale, row_src, T, H / kBlock, (int)rows_total,
                        a_scale);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }

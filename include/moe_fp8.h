@@ -161,12 +161,15 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
  * moe_act_requant — SiLU(gate) * up, re-quantised to E4M3 with fresh 1x128
  * scales (reading: SiLU and the gate/up order are not on the pages).  For
  * every valid row m and j in [0, I):
- *   v = silu(h[m, j]) * h[m, I + j],  silu(g) = g / (1 + exp(-g))  (fp32)
+ *   v = silu(h[m, j]) * h[m, I + j],  silu(g) = g / (1 + exp(-g))
+ *       (fp32; exp and the reciprocal from the hardware, ~1 ulp each)
  *   per block jb of 128 columns: s = amax|v| / 448 (1 if amax == 0)
  *   q[m, j] = e4m3_rne(clamp(v / s, -448, 448)); q_scale[jb, m] = s
+ *       (v / s correctly rounded in fp32, as the quantiser's decision)
  *
  *   h        [rows_total, 2I] bf16
  *   q        [rows_total, I] e4m3     q_scale [I/128, rows_total] f32
+ * I must be a multiple of 128 (MOE_UNSUPPORTED_SHAPE otherwise).
  * status_dev is accepted for uniformity and not written.
  */
 moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
