@@ -9,13 +9,13 @@
 // capturable) mode a fixed-capacity masked layout.
 //
 // Kernels (all stream-ordered, fixed grids, no host reads):
-//   layout_count   one block per chunk of 4096 flat entries: LDS histogram
+//   layout_count   one block per chunk of 1024 flat entries: LDS histogram
+//                  (ballot-grouped atomics); also row_src / row_expert <- -1
 //   layout_scan    one block: per-chunk exclusive bases, counts, offsets
-//   layout_fill    row_src / row_expert <- -1 over the whole buffer
 //   layout_rank    one block per chunk: wave-ballot ranks in flat order,
 //                  writes slot_of, row_src, row_expert
-//   permute_rows   one wave per source token: reads x[t] once, writes it to
-//                  each of the token's slots (16-byte accesses)
+//   permute_rows   one wave per piece of a source row: reads x[t] once,
+//                  writes it to each of the token's slots (16-byte accesses)
 //   permute_scales the matching scales, 64 slots per workgroup transposed
 //                  through LDS (contiguous reads and stores)
 #include "device_common.hpp"
@@ -23,27 +23,55 @@
 namespace moe {
 
 constexpr int kLayoutThreads = 256;
-constexpr int kLayoutRounds = 16;
+constexpr int kLayoutRounds = 4;
 constexpr int kChunk = kLayoutThreads * kLayoutRounds;   // flat entries per block
 constexpr int kWaves = kLayoutThreads / 64;
+constexpr int kScanThreads = 1024;
 
+// Lanes of the wave whose key equals this lane's (ballots over the key bits).
+__device__ __forceinline__ unsigned long long match_key(int key, int key_bits) {
+  unsigned long long m = __ballot(1);
+  for (int b = 0; b < key_bits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const unsigned long long bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+// Per-chunk expert histogram.  A chunk's entries are requested at once;
+// lanes of a wave with the same expert are grouped by ballots and the lowest
+// of them adds the group size, so there is one LDS atomic per expert per
+// wave and round.  The same grid also sets row_src / row_expert to -1 over
+// the whole buffer (layout_rank, the next kernel, overwrites filled rows).
 __global__ __launch_bounds__(kLayoutThreads) void layout_count(
-    const int32_t* __restrict__ idx, long long F, int E,
-    int32_t* __restrict__ chunk_counts, int32_t* __restrict__ status) {
+    const int32_t* __restrict__ idx, long long F, int E, int key_bits,
+    int32_t* __restrict__ chunk_counts, int32_t* __restrict__ row_src,
+    int32_t* __restrict__ row_expert, int rows_total, int32_t* __restrict__ status) {
   extern __shared__ int32_t hist[];
-  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-  long long base = (long long)blockIdx.x * kChunk;
-  int bad = 0;
+  const long long base = (long long)blockIdx.x * kChunk;
+  int ev[kLayoutRounds];
+#pragma unroll
   for (int r = 0; r < kLayoutRounds; ++r) {
-    long long f = base + r * kLayoutThreads + threadIdx.x;
-    if (f < F) {
-      int e = idx[f];
-      if (e >= 0 && e < E)
-        atomicAdd(&hist[e], 1);
-      else if (e != -1)
-        bad = 1;
-    }
+    const long long f = base + r * kLayoutThreads + threadIdx.x;
+    ev[r] = f < F ? idx[f] : -1;
+  }
+  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < rows_total;
+       i += (long long)gridDim.x * blockDim.x) {
+    row_src[i] = -1;
+    row_expert[i] = -1;
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << (threadIdx.x & 63)) - 1ull;
+  int bad = 0;
+#pragma unroll
+  for (int r = 0; r < kLayoutRounds; ++r) {
+    const int e = ev[r];
+    const bool valid = e >= 0 && e < E;
+    if (!valid && e != -1) bad = 1;
+    const unsigned long long m = match_key(valid ? e + 1 : 0, key_bits);
+    if (valid && (m & lt) == 0) atomicAdd(&hist[e], __popcll(m));
   }
   bad = __syncthreads_or(bad);
   for (int i = threadIdx.x; i < E; i += blockDim.x)
@@ -51,46 +79,72 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count(
   if (bad && threadIdx.x == 0) atomicOr(status, MOE_ERR_BAD_EXPERT);
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_scan(
-    const int32_t* __restrict__ chunk_counts, int nchunks, int E, int layout,
+// Exclusive prefix over chunks of every expert's count (chunk_base), the
+// totals (counts) and the segment starts (offsets).  Each expert gets a
+// group of `group` lanes (64 when E <= 16); a lane sums its own range of
+// chunks, the group scans the partial sums with shuffles, and the lane then
+// writes its range's bases.  Offsets are a block-wide scan over experts of
+// the totals rounded up to align_m (contiguous) or e * cap (masked).
+__global__ __launch_bounds__(kScanThreads) void layout_scan(
+    const int32_t* __restrict__ chunk_counts, int nchunks, int E, int group, int layout,
     int align_m, int cap, int32_t* __restrict__ chunk_base,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  extern __shared__ int32_t tot[];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0;
-    for (int b = 0; b < nchunks; ++b) {
-      long long i = (long long)b * E + e;
-      chunk_base[i] = s;
-      s += chunk_counts[i];
+  __shared__ int32_t tot[MOE_MAX_EXPERTS];
+  __shared__ long long wsum[kScanThreads / 64];
+  const int lg = threadIdx.x % group, grp = threadIdx.x / group;
+  const int ngrp = kScanThreads / group;
+  const int per = (nchunks + group - 1) / group;
+  const int b0 = min(lg * per, nchunks), b1 = min(b0 + per, nchunks);
+  for (int e0 = 0; e0 < E; e0 += ngrp) {   // uniform trip count: shuffles stay converged
+    const int e = e0 + grp;
+    const bool live = e < E;
+    int local = 0;
+    if (live) {
+#pragma unroll 8
+      for (int b = b0; b < b1; ++b) local += chunk_counts[(long long)b * E + e];
     }
-    counts[e] = s;
-    tot[e] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long o = 0;
-    for (int e = 0; e < E; ++e) {
-      if (layout == MOE_LAYOUT_MASKED) {
-        offsets[e] = (int32_t)((long long)e * cap);
-      } else {
-        offsets[e] = (int32_t)(o > 0x7fffffffLL ? 0x7fffffffLL : o);
-        o += ((long long)tot[e] + align_m - 1) / align_m * align_m;
+    int incl = local;
+    for (int d = 1; d < group; d <<= 1) {
+      const int v = __shfl_up(incl, d, group);
+      if (lg >= d) incl += v;
+    }
+    if (live) {
+      int run = incl - local;
+#pragma unroll 8
+      for (int b = b0; b < b1; ++b) {
+        const long long i = (long long)b * E + e;
+        const int c = chunk_counts[i];
+        chunk_base[i] = run;
+        run += c;
+      }
+      if (lg == group - 1) {
+        counts[e] = incl;
+        tot[e] = incl;
       }
     }
-    if (layout == MOE_LAYOUT_MASKED)
-      offsets[E] = (int32_t)((long long)E * cap);
-    else
-      offsets[E] = (int32_t)(o > 0x7fffffffLL ? 0x7fffffffLL : o);
   }
-}
-
-__global__ void layout_fill(int32_t* __restrict__ row_src,
-                            int32_t* __restrict__ row_expert, int rows_total) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-       i < rows_total; i += (long long)gridDim.x * blockDim.x) {
-    row_src[i] = -1;
-    row_expert[i] = -1;
+  __syncthreads();
+  const int e = threadIdx.x;   // E <= MOE_MAX_EXPERTS == kScanThreads
+  if (layout == MOE_LAYOUT_MASKED) {
+    if (e < E) offsets[e] = (int32_t)((long long)e * cap);
+    if (e == 0) offsets[E] = (int32_t)((long long)E * cap);
+    return;
   }
+  const long long mine =
+      e < E ? ((long long)tot[e] + align_m - 1) / align_m * align_m : 0;
+  long long incl = mine;
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long v = __shfl_up(incl, d, 64);
+    if ((threadIdx.x & 63) >= d) incl += v;
+  }
+  if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  long long before = 0;
+  for (int w = 0; w < (threadIdx.x >> 6); ++w) before += wsum[w];
+  incl += before;
+  const long long lim = 0x7fffffffLL;
+  if (e < E) offsets[e] = (int32_t)(incl - mine > lim ? lim : incl - mine);
+  if (e == E - 1) offsets[E] = (int32_t)(incl > lim ? lim : incl);
 }
 
 // Stable rank of every flat entry f = t*K + k inside its expert.  Each block
@@ -120,18 +174,20 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank(
   const int wave = threadIdx.x >> 6;
   const unsigned long long lt = (1ull << lane) - 1ull;
   long long base = (long long)blockIdx.x * kChunk;
+  int ev[kLayoutRounds];
+#pragma unroll
+  for (int r = 0; r < kLayoutRounds; ++r) {
+    const long long f = base + r * kLayoutThreads + threadIdx.x;
+    ev[r] = f < F ? idx[f] : -1;
+  }
   int overflow = 0;
+#pragma unroll
   for (int r = 0; r < kLayoutRounds; ++r) {
     long long f = base + r * kLayoutThreads + threadIdx.x;
-    int e = f < F ? idx[f] : -1;
+    int e = ev[r];
     bool valid = e >= 0 && e < E;
     int key = valid ? e + 1 : 0;
-    unsigned long long m = ~0ull;
-    for (int b = 0; b < key_bits; ++b) {
-      bool bit = (key >> b) & 1;
-      unsigned long long bal = __ballot(bit);
-      m &= bit ? bal : ~bal;
-    }
+    const unsigned long long m = match_key(key, key_bits);
     int lane_rank = __popcll(m & lt);
     int group = __popcll(m);
     bool leader = (m & lt) == 0;
@@ -176,37 +232,45 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank(
 // One wave per source token: the token's row is read from HBM once (16-byte
 // loads, 64 lanes side by side, all of a row's loads in flight together)
 // and written to every slot it was given.
-constexpr int kPermChunks = 8;   // 16-byte chunks per lane per pass (H <= 8192 in one pass)
+#ifndef MOE_PERM_CHUNKS
+#define MOE_PERM_CHUNKS 2
+#endif
+constexpr int kPermChunks = MOE_PERM_CHUNKS;   // 16-byte chunks per lane
 
+// One wave per piece of a source row: the row's H/16 chunks are cut into
+// `pieces` pieces of at most `plen` <= 64 * kPermChunks chunks (H = 7168:
+// four pieces of 112), so a row is read once by a few waves that each hold
+// their piece in registers and store it to every slot of the token.  The
+// token's slots and the piece are requested together; only the stores wait
+// for the slots.
 __global__ __launch_bounds__(256) void permute_rows(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ slot_of, int T, int K, int H,
-    int rows_total, uint8_t* __restrict__ a) {
+    int pieces, int plen, int rows_total, uint8_t* __restrict__ a) {
   const int lane = threadIdx.x & 63;
-  const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long t = w / pieces;
   if (t >= T) return;
-  // the token's slots and its first chunks are requested together; only the
-  // stores wait for the slots
-  const int s = lane < K ? slot_of[t * K + lane] : -1;
   const int n16 = H >> 4;
+  const int c0 = (int)(w - t * pieces) * plen;
+  const int cend = min(c0 + plen, n16);
+  const int s = lane < K ? slot_of[t * K + lane] : -1;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
-  for (int c0 = lane; c0 < n16; c0 += 64 * kPermChunks) {
-    uint4 v[kPermChunks];
+  uint4 v[kPermChunks];
+#pragma unroll
+  for (int u = 0; u < kPermChunks; ++u) {
+    const int c = c0 + lane + u * 64;
+    v[u] = src[c < cend ? c : c0];   // past the piece: re-read its first chunk, not stored
+  }
+  unsigned long long m = __ballot(s >= 0 && s < rows_total);
+  while (m) {
+    const int k = __ffsll((long long)m) - 1;
+    m &= m - 1;
+    const int slot = __builtin_amdgcn_readlane(s, k);
+    uint4* dst = reinterpret_cast<uint4*>(a + (long long)slot * H);
 #pragma unroll
     for (int u = 0; u < kPermChunks; ++u) {
-      const int c = c0 + u * 64;
-      v[u] = src[c < n16 ? c : 0];   // past the row: re-read chunk 0, not stored
-    }
-    unsigned long long m = __ballot(s >= 0 && s < rows_total);
-    while (m) {
-      const int k = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const int slot = __builtin_amdgcn_readlane(s, k);
-      uint4* dst = reinterpret_cast<uint4*>(a + (long long)slot * H);
-#pragma unroll
-      for (int u = 0; u < kPermChunks; ++u) {
-        const int c = c0 + u * 64;
-        if (c < n16) dst[c] = v[u];
-      }
+      const int c = c0 + lane + u * 64;
+      if (c < cend) dst[c] = v[u];
     }
   }
 }
@@ -251,6 +315,15 @@ static int key_bits_for(int E) {
   int b = 0;
   while ((1 << b) < E + 1) ++b;
   return b;
+}
+
+// Lanes per expert in layout_scan: the block's 1024 threads shared out over
+// the experts (rounded up to a power of two), at most one wave per expert.
+static int scan_group(int E) {
+  int p = 1;
+  while (p < E) p <<= 1;
+  const int g = kScanThreads / p;
+  return g > 64 ? 64 : (g < 1 ? 1 : g);
 }
 
 static long long n_chunks(int T, int K) {
@@ -301,19 +374,12 @@ extern "C" moe_status_t moe_dispatch_layout(
   int32_t* chunk_base = chunk_counts + (nc < 1 ? 1 : nc) * E;
   const int cap = layout == MOE_LAYOUT_MASKED ? rows : 0;
 
-  if (nc > 0)
-    hipLaunchKernelGGL(layout_count, dim3((unsigned)nc), dim3(kLayoutThreads),
-                       E * sizeof(int32_t), st, topk_idx, F, E, chunk_counts,
-                       status_dev);
-  hipLaunchKernelGGL(layout_scan, dim3(1), dim3(kLayoutThreads),
-                     E * sizeof(int32_t), st, chunk_counts, (int)nc, E, layout,
-                     align_m, cap, chunk_base, counts, offsets);
-  if (rows_total > 0) {
-    long long blocks = (rows_total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(layout_fill, dim3((unsigned)blocks), dim3(256), 0, st,
-                       row_src, row_expert, (int)rows_total);
-  }
+  const int ncl = (int)(nc < 1 ? 1 : nc);   // count always runs: it also clears row_src
+  hipLaunchKernelGGL(layout_count, dim3((unsigned)ncl), dim3(kLayoutThreads),
+                     E * sizeof(int32_t), st, topk_idx, F, E, key_bits_for(E), chunk_counts,
+                     row_src, row_expert, (int)rows_total, status_dev);
+  hipLaunchKernelGGL(layout_scan, dim3(1), dim3(kScanThreads), 0, st, chunk_counts, ncl, E,
+                     scan_group(E), layout, align_m, cap, chunk_base, counts, offsets);
   if (nc > 0)
     hipLaunchKernelGGL(layout_rank, dim3((unsigned)nc), dim3(kLayoutThreads),
                        (2 + kWaves) * E * sizeof(int32_t), st, topk_idx, F, K,
@@ -321,8 +387,12 @@ extern "C" moe_status_t moe_dispatch_layout(
                        offsets, chunk_base, slot_of, row_src, row_expert,
                        status_dev);
   if (T > 0 && rows_total > 0) {
-    hipLaunchKernelGGL(permute_rows, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x,
-                       slot_of, T, K, H, (int)rows_total, a);
+    const int n16 = H / 16;
+    const int pieces = (n16 + 64 * kPermChunks - 1) / (64 * kPermChunks);
+    const int plen = (n16 + pieces - 1) / pieces;
+    const long long waves = (long long)T * pieces;
+    hipLaunchKernelGGL(permute_rows, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, x,
+                       slot_of, T, K, H, pieces, plen, (int)rows_total, a);
     hipLaunchKernelGGL(permute_scales, dim3((unsigned)((rows_total + kScTile - 1) / kScTile)),
                        dim3(256), 0, st, x_scale, row_src, T, H / kBlock, (int)rows_total,
                        a_scale);

@@ -28,8 +28,9 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes():
     lib = _lib.load()
-    # one int32 histogram and one int32 base per (chunk of 4096 entries, expert)
-    assert lib.moe_layout_workspace_bytes(65536, 8, 9) == 2 * 128 * 9 * 4
+    # one int32 histogram and one int32 base per (chunk of 1024 entries, expert)
+    assert lib.moe_layout_workspace_bytes(65536, 8, 9) == 2 * 512 * 9 * 4
+    assert lib.moe_layout_workspace_bytes(129, 8, 9) == 2 * 2 * 9 * 4
     assert lib.moe_layout_workspace_bytes(1, 1, 4) == 2 * 1 * 4 * 4
     assert lib.moe_layout_workspace_bytes(0, 8, 4) == 2 * 1 * 4 * 4
     assert lib.moe_layout_workspace_bytes(-1, 8, 4) == 0

@@ -184,6 +184,49 @@ def test_layout_large_expert_count(gpu):
     _check_layout(cfg, idx, x, xs, rows)
 
 
+def _random_routing(g, T, K, E, fill=1.0):
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        if g.uniform() > fill:
+            continue
+        n = int(g.integers(1, min(K, E) + 1))
+        idx[t, g.permutation(K)[:n]] = g.choice(E, size=n, replace=False)
+    return idx
+
+
+# (T, K, E, H, layout, rows or capacity): empty input into a non-empty
+# buffer, a single expert, the maximum expert count (one scan lane per
+# expert, the masked end offset), rows whose 16-byte chunks split unevenly
+# into permute pieces (H = 4224: 264 chunks, two pieces of 132), and a
+# masked capacity that overflows.
+EDGE_LAYOUTS = [
+    (0, 8, 9, 256, moe.LAYOUT_CONTIGUOUS, 300),
+    (0, 8, 9, 256, moe.LAYOUT_MASKED, 4),
+    (50, 4, 1, 128, moe.LAYOUT_CONTIGUOUS, 50 * 4 + 127),
+    (700, 8, 1024, 4224, moe.LAYOUT_MASKED, 4),
+    (700, 8, 1024, 4224, moe.LAYOUT_CONTIGUOUS, None),
+    (2500, 3, 7, 4224, moe.LAYOUT_CONTIGUOUS, None),
+    (2500, 6, 33, 384, moe.LAYOUT_MASKED, 200),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_LAYOUTS, ids=lambda c: f"T{c[0]}K{c[1]}E{c[2]}H{c[3]}L{c[4]}")
+def test_layout_edge_shapes(gpu, case):
+    from dataclasses import replace
+    T, K, E, H, layout, rows = case
+    g = np.random.default_rng(T * 131 + E)
+    idx = _random_routing(g, T, K, E, fill=0.9)
+    if rows is None:
+        rows = int((idx >= 0).sum()) + E * 127
+    cfg = replace(CONFIGS[1], E=E, H=H, T=T, K=K, layout=layout,
+                  capacity=rows if layout == moe.LAYOUT_MASKED else 0)
+    x = g.integers(0, 256, (T, H), dtype=np.uint8)
+    x[(x & 0x7F) == 0x7F] = 0
+    xs = g.uniform(0.5, 2, (T, H // 128)).astype(np.float32)
+    log(f"layout edge: T={T} K={K} E={E} H={H} layout={layout} rows={rows}")
+    _check_layout(cfg, idx, x, xs, rows)
+
+
 # --------------------------------------------------------------- GEMM
 def _run_gemm(a, sa_rows, w, sw, offsets, counts, rows_total):
     """Upload, run moe_grouped_gemm_fp8, return bf16 bits [rows_total, N]."""
