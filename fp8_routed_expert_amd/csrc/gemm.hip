@@ -10,16 +10,22 @@
 //                         * sum_{k in kb} a[m, k] * w[e, n, k] )
 //
 // Design (gfx950):
-//   * A workgroup computes a BM x BN = 128 x 128 tile of c with 4 waves; each
-//     wave owns a 64 x 64 sub-tile of 4 x 4 MFMA subtiles of 16 x 16.  Two
-//     workgroups share a CU (64 KB of LDS each), i.e. two waves per SIMD.
+//   * Large problems: a workgroup computes a 256 x 256 tile of c with 8 waves
+//     of 128 x 64 (two waves per SIMD, one workgroup per CU, two 64 KB LDS
+//     stages).  Small problems: 128 x 128 tiles of 4 waves of 64 x 64, two
+//     workgroups per CU.  A wave's sub-tile is a grid of 16 x 16 MFMA
+//     subtiles.
 //   * K advances one 128-wide scale block per step.  v_mfma_f32_16x16x128
 //     _f8f6f4 consumes exactly one block per subtile, so each block's raw
 //     product comes out of a single MFMA issued with a zero accumulator and
 //     is promoted into the fp32 accumulator with one FMA by the combined
-//     scale f = sa[kb, m] * sw[e, nb, kb].  The MFMAs of subtile row i are
-//     issued while the FMAs promote row i - 1, so matrix-core and VALU work
-//     overlap; the accumulators stay in VGPRs.
+//     scale f = sa[kb, m] * sw[e, nb, kb].  The MFMA computes the transposed
+//     product (weights as the first operand), so a lane's four outputs of a
+//     subtile are four columns of one row: one row scale per lane.  Each
+//     MFMA of subtile row i is followed in issue order by the four FMAs that
+//     promote the same column of row i - 1 (whose product is complete), so
+//     one wave overlaps its own matrix-core and VALU work; the accumulators
+//     stay in VGPRs.
 //   * A and B tiles (rows x 128 bytes) go from global memory straight into
 //     LDS with buffer_load_dwordx4 ... lds (no staging registers), two
 //     stages deep: the next step's loads are in flight while the current
@@ -27,10 +33,11 @@
 //     unrolled by two, so the compiler can see that reading one stage never
 //     waits on the loads filling the other; the step barrier orders LDS only
 //     and the tile loads are waited for explicitly.  Inside every 16-row
-//     group the 16-byte chunks are XOR-permuted by ((row >> 1) & 7) -- chosen
-//     through the per-lane global offset, since each load instruction fills
-//     1 KB of LDS contiguously -- so a fragment read (16 rows x 16 bytes per
-//     lane group) touches all 64 banks once.
+//     group the 16-byte chunks are XOR-permuted by (row & 7) ^ ((row >> 3) & 1)
+//     -- chosen through the per-lane global offset, since each load
+//     instruction fills 1 KB of LDS contiguously -- which measured free of
+//     bank conflicts for the fragment reads (4 LDS cycles per 1 KB read);
+//     the (row >> 1) & 7 permutation measured a 2-way conflict.
 //   * Row scales are K-block-major (contiguous per block), prefetched one
 //     step ahead in registers and staged in LDS; the weight-block scale of a
 //     wave's columns is a scalar load.
@@ -40,11 +47,14 @@
 //     exit at once; nothing is read back on the host and the launch can be
 //     captured in a hipGraph.  Buffer descriptors bound every tile load, so
 //     rows past the end of the buffer read as zero (and are never stored).
-//   * Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
-//     The workgroup id is remapped so that each XCD walks its own contiguous
-//     share of the tile list, which is ordered in groups of GM m-tiles x all
-//     n-tiles (m fastest): the tiles an XCD runs at the same time then share
-//     a few A panels and a few weight panels in that XCD's L2.
+//   * Tile order and the 8 XCDs (each with its own L2): workgroup w runs on
+//     XCD w mod 8 and takes tile w of a list ordered in groups of GM m-tiles
+//     x all n-tiles (m fastest).  With GM = 2 the 32 tiles one XCD runs at
+//     a time are 8 m-tiles x 4 n-tiles (12 distinct panels per 64 panel
+//     loads in its L2), and all XCDs work in the same few groups, so the
+//     current expert's weights are shared through the memory-side cache.
+//     This measured a few percent faster than giving each XCD a contiguous
+//     share of the list (XCDs then stream different experts' weights).
 #include "device_common.hpp"
 
 namespace moe {
@@ -83,10 +93,11 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
 }
 
 // Physical position of logical 16-byte chunk c of tile row r: chunks are
-// XOR-permuted by ((r >> 1) & 7), so the 16 rows a fragment read touches at
-// once (16 lanes x 16 bytes) cover all 64 LDS banks exactly once: rows of
-// equal parity sit in the same half of the banks and get 8 distinct chunks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// XOR-permuted by (r & 7) ^ ((r >> 3) & 1).  A fragment read has lane
+// (q, g) read chunk 2g (then 2g + 1) of row 16 b + q; with this permutation
+// the LDS serves it without bank conflicts (4 cycles per 1 KB wave read on
+// gfx950, against 8 for the (r >> 1) & 7 and r & 7 permutations).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // 32 bytes of row `row` of a swizzled tile: logical 16-byte chunks 2g, 2g+1.
 __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int g) {
@@ -158,17 +169,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   __shared__ __attribute__((aligned(16))) float sS0[BM];
   __shared__ __attribute__((aligned(16))) float sS1[BM];
 
-  // ---- which tile: XCD-aware remap, then grouped order over the tile list
+  // ---- which tile: grouped order over the tile list (see the XCD note above)
   const int n_tiles = N / BN;
   int e_sel, row0 = 0, row_end = 0;
   const int total_m = find_mtile<BM>(offsets, counts, E, rows_total, 0x7fffffff, e_sel,
                                      row0, row_end);
   const int total = total_m * n_tiles;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int q = (total + kXcds - 1) / kXcds;   // real tiles per XCD
-  if (slot >= q) return;
-  const int logical = xcd * q + slot;
+  const int logical = blockIdx.x;
   if (logical >= total) return;
   const int group_size = GM * n_tiles;
   const int grp = logical / group_size;
@@ -210,17 +217,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // Row scales (K-block-major, so a tile's rows are contiguous) are loaded
   // into registers one step ahead by the first BM threads and written to the
   // stage's scale block at the end of the step; rows past the buffer are
-  // clamped and only feed rows that are never stored.  In LDS row
-  // wm*WM + i*16 + q sits at ((wm*16 + q) * MI + i), so a lane -- whose
-  // outputs all belong to row q of each of its MI subtiles -- reads its MI
-  // scales as one contiguous run.  The weight-block scale of this wave's
+  // clamped and only feed rows that are never stored.  In LDS the scale of
+  // row wm*WM + i*16 + q sits at ((i/4) * (BM/WM) * 16 + wm*16 + q) * 4 +
+  // i%4, so a lane -- whose outputs all belong to row q of each of its MI
+  // subtiles -- reads its MI scales as MI/4 float4s, and the 16 lanes of a
+  // read cover one contiguous 256-byte run.  The weight-block scale of this wave's
   // columns is one wave-uniform value per step, read with a scalar load one
   // step ahead.
   const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * Kb;
   const bool row_owner = tid < BM;
   int sa_row = row0 + (row_owner ? tid : 0);
   sa_row = sa_row < rows_total ? sa_row : rows_total - 1;
-  const int sa_pos = ((tid / WM) * 16 + (tid & 15)) * MI + (tid % WM) / 16;
+  const int sa_pos =
+      ((((tid % WM) / 16) >> 2) * (BM / WM) * 16 + (tid / WM) * 16 + (tid & 15)) * 4 +
+      (((tid % WM) / 16) & 3);
 
   // Every wave issues the same CH_PER_WAVE tile-chunk loads per stage.
   auto issue = [&](int kb, uint8_t* stA, uint8_t* stB) {
@@ -241,6 +251,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       }
     }
   };
+
 
   v4f acc[MI][NJ];
 #pragma unroll
@@ -269,7 +280,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     float fs[MI];
 #pragma unroll
     for (int i4 = 0; i4 < MI; i4 += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(&tS[(wm * 16 + r16) * MI + i4]);
+      const float4 v = *reinterpret_cast<const float4*>(
+          &tS[((i4 >> 2) * (BM / WM) * 16 + wm * 16 + r16) * 4]);
       fs[i4] = v.x; fs[i4 + 1] = v.y; fs[i4 + 2] = v.z; fs[i4 + 3] = v.w;
     }
     float sa_next = 0.f;
@@ -311,6 +323,18 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
         fprev = fcur;
+      }
+      // issue order inside the row: the next A fragment's LDS reads, then
+      // each MFMA of row i followed by the four FMAs that promote the same
+      // column of row i - 1 (left to itself the scheduler puts the FMAs
+      // first, where they wait for the MFMAs issued just before them)
+      if (i > 0 && i < MI) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -377,7 +401,7 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 // per CU).  kTag keeps the gate/up (1) and down (2) projections as separate
 // kernel symbols so that profiles attribute time per projection.
 #ifndef MOE_GEMM_BIG
-#define MOE_GEMM_BIG 256, 256, 128, 64, 4
+#define MOE_GEMM_BIG 256, 256, 128, 64, 2
 #endif
 #ifndef MOE_GEMM_SMALL
 #define MOE_GEMM_SMALL 128, 128, 64, 64, 4
