@@ -14,6 +14,11 @@ Prints one JSON line: MoE-layer FP8 TFLOP/s (value), token-rows/s, the
 fraction of the FP8 MFMA peak, per-kernel times, the roofline of the dominant
 kernel (GEMM1, events on the launch stream) and the CPU oracle timed on a
 bounded sample of the same workload.
+
+Other workloads (--config 1-5) are the decode shares; --graph replays the
+step from one hipGraph (the decode mode), and --flush-mib writes a scratch
+buffer between steps, outside the timed span, so that weights are streamed
+from HBM rather than found in the memory-side cache.
 """
 
 import argparse
@@ -109,6 +114,11 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="source tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step's launches in one hipGraph and time replays")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write a scratch buffer of this many MiB before every timed step "
+                         "(outside the timed span) to evict the memory-side cache")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first "
                          "(reference for scaling HBM byte counters)")
@@ -178,36 +188,73 @@ def main():
         if evs is not None:
             evs[5].record()
 
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()                      # untimed launch on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def run_step(evs=None):
+        if graph is None:
+            step(evs)
+            return
+        if evs is not None:
+            evs[0].record()
+        graph.replay()
+        if evs is not None:
+            evs[-1].record()
+
     for _ in range(args.warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
     st = int(layer.status.item())
     if st != 0:
         raise RuntimeError(f"device status word {st} after warm-up")
 
+    scratch = None
+    if args.flush_mib:
+        scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        if scratch is not None:
+            scratch.fill_(k & 0xff)     # outside the events of step k
+        run_step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    step_ms = [events[k][0].elapsed_time(events[k][5]) for k in range(args.steps)]
+    # wall clock over exactly K steps, unless flushes sit between them: then
+    # the sum of the steps' own event spans
+    ms = (t1 - t0) * 1e3 / args.steps if scratch is None else float(np.mean(step_ms))
     names = ["dispatch_layout", "gemm1_gate_up", "act_requant", "gemm2_down", "combine"]
-    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
-                             for k in range(args.steps)])) for i, n in enumerate(names)}
+    per = None
+    if graph is None:
+        per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
+                                 for k in range(args.steps)])) for i, n in enumerate(names)}
 
     flops1 = 2.0 * R * (2 * I) * H
     flops2 = 2.0 * R * H * I
     flops = flops1 + flops2
-    hb = H // 128
+    hb, ib = H // 128, I // 128
     bytes_perm = (T + R) * (H + 4 * hb) + T * K * 4
-    bytes_act = R * (4 * I + I + 4 * (I // 128))
+    bytes_act = R * (4 * I + I + 4 * ib)
     bytes_comb = R * 2 * H + T * 2 * H + T * K * 8
+    # GEMM bytes: weights (and scales) of experts with rows, A and its scales, C
+    live = int(np.count_nonzero(np.bincount(idx[idx >= 0], minlength=E)))
+    bytes_g1 = live * (2 * I * H + (2 * I // 128) * hb * 4) + R * (H + 4 * hb) + R * 2 * I * 2
+    bytes_g2 = live * (H * I + hb * ib * 4) + R * (I + 4 * ib) + R * H * 2
     tflops = flops / (ms * 1e-3) / 1e12
-    g1 = flops1 / (per["gemm1_gate_up"] * 1e-3) / 1e12
     launch_key = f"{cfg.name}:R={R}:rows={rows}"
     traffic = stored_traffic(launch_key)
+    pct = lambda q: round(float(np.percentile(step_ms, q)), 4)
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -225,21 +272,40 @@ def main():
                                f"{T} source tokens, top-{K}, {R} routed rows, "
                                f"{'masked' if cfg.layout else 'contiguous'} layout",
                    "experts": E, "hidden": H, "intermediate": I, "tokens": T,
-                   "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total},
+                   "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total,
+                   "experts_with_rows": live},
+        "timing": {"mode": "hipgraph replay" if graph is not None else "eager launches",
+                   "cache_flush_mib": args.flush_mib,
+                   "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90)},
         "mfma_peak_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
         "token_rows_per_s": round(R / (ms * 1e-3), 1),
-        "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
-        "per_kernel_rate": {
+    }
+    if per is not None:
+        g1 = flops1 / (per["gemm1_gate_up"] * 1e-3) / 1e12
+        g1_gbs = bytes_g1 / (per["gemm1_gate_up"] * 1e-3) / 1e9
+        result["per_kernel_ms"] = {k: round(v, 4) for k, v in per.items()}
+        result["per_kernel_rate"] = {
             "gemm1_tflops": round(g1, 1),
+            "gemm1_gbs": round(g1_gbs, 1),
             "gemm2_tflops": round(flops2 / (per["gemm2_down"] * 1e-3) / 1e12, 1),
+            "gemm2_gbs": round(bytes_g2 / (per["gemm2_down"] * 1e-3) / 1e9, 1),
             "dispatch_gbs": round(bytes_perm / (per["dispatch_layout"] * 1e-3) / 1e9, 1),
             "act_gbs": round(bytes_act / (per["act_requant"] * 1e-3) / 1e9, 1),
             "combine_gbs": round(bytes_comb / (per["combine"] * 1e-3) / 1e9, 1),
-        },
-        "roofline": {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "mfma",
-                     "achieved": round(g1, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g1 / FP8_PEAK_TFLOPS, 4), "traffic": traffic},
-    }
+        }
+        # GEMM1 dominates every workload; below the ridge point (peak flop/s over
+        # peak bytes/s) its bound is weight streaming from HBM
+        ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if flops1 / bytes_g1 >= ridge:
+            result["roofline"] = {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "mfma",
+                                  "achieved": round(g1, 2), "peak": FP8_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(g1 / FP8_PEAK_TFLOPS, 4),
+                                  "traffic": traffic}
+        else:
+            result["roofline"] = {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "hbm",
+                                  "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": traffic}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(cfg, idx, w, args.cpu_tokens)

@@ -26,21 +26,22 @@
 //     promote the same column of row i - 1 (whose product is complete), so
 //     one wave overlaps its own matrix-core and VALU work; the accumulators
 //     stay in VGPRs.
-//   * A and B tiles (rows x 128 bytes) go from global memory straight into
-//     LDS with buffer_load_dwordx4 ... lds (no staging registers), two
-//     stages deep: the next step's loads are in flight while the current
-//     step is multiplied.  Each stage is its own LDS object and the K loop is
-//     unrolled by two, so the compiler can see that reading one stage never
-//     waits on the loads filling the other; the step barrier orders LDS only
-//     and the tile loads are waited for explicitly.  Inside every 16-row
+//   * A and B tiles (rows x 128 bytes) and the tile's row scales go from
+//     global memory straight into LDS with buffer_load ... lds (no staging
+//     registers), ST stages deep (ST - 1 k-blocks in flight while one is
+//     multiplied; both tile configurations use ST = 2: three and four
+//     stages, with one workgroup per CU, measured slower).  Each stage is
+//     its own LDS object and the K loop is unrolled by ST, so the compiler
+//     can see that reading one stage never waits on the loads filling
+//     another; the step barrier orders LDS only and the loads are waited for
+//     explicitly with vmcnt.  Inside every 16-row
 //     group the 16-byte chunks are XOR-permuted by (row & 7) ^ ((row >> 3) & 1)
 //     -- chosen through the per-lane global offset, since each load
 //     instruction fills 1 KB of LDS contiguously -- which measured free of
 //     bank conflicts for the fragment reads (4 LDS cycles per 1 KB read);
 //     the (row >> 1) & 7 permutation measured a 2-way conflict.
-//   * Row scales are K-block-major (contiguous per block), prefetched one
-//     step ahead in registers and staged in LDS; the weight-block scale of a
-//     wave's columns is a scalar load.
+//   * Row scales are K-block-major (contiguous per block); the weight-block
+//     scale of a wave's columns is a scalar load one step ahead.
 //   * Tiles come from device-side offsets/counts: m-tiles are numbered
 //     expert by expert (ceil(valid rows / BM) per expert), so the grid is
 //     fixed by the buffer size alone and workgroups past the last real tile
@@ -55,6 +56,8 @@
 //     current expert's weights are shared through the memory-side cache.
 //     This measured a few percent faster than giving each XCD a contiguous
 //     share of the list (XCDs then stream different experts' weights).
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace moe {
@@ -134,7 +137,7 @@ __device__ __forceinline__ int find_mtile(const int32_t* offsets, const int32_t*
   return acc;
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int kTag>
+template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
@@ -150,24 +153,37 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   constexpr int A_CHUNKS = BM / 8;                   // 1 KB LDS chunks per stage
   constexpr int B_CHUNKS = BN / 8;
   constexpr int CH_PER_WAVE = (A_CHUNKS + B_CHUNKS) / NW;
+  constexpr int LPS = CH_PER_WAVE + 1;   // loads per wave and step: tile chunks + row scales
   static_assert((A_CHUNKS + B_CHUNKS) % NW == 0, "chunks must split evenly");
   static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
   static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
-  static_assert(BM <= NT, "one thread per tile row for the row scales");
+  static_assert(BM % 64 == 0 && BM / 64 <= NW, "one scale load of 64 rows per wave");
   static_assert(MI % 4 == 0, "row scales are read four at a time");
   static_assert(CH_PER_WAVE % 2 == 0 && A_CHUNKS % 2 == 0, "chunk parity is static");
+  static_assert(ST >= 2 && ST <= 4, "pipeline depth");
+  static_assert((ST - 2) * LPS < 64, "vmcnt range");
   (void)kTag;
 
-  // one LDS object per stage: the K loop below is unrolled by two so
-  // every access names its stage statically, which lets the compiler see
-  // that reading one stage does not wait on the loads filling another.
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * kBK];
-  // per stage: a_scale of the BM rows
-  __shared__ __attribute__((aligned(16))) float sS0[BM];
-  __shared__ __attribute__((aligned(16))) float sS1[BM];
+  // One LDS object per stage (A rows, B rows, row scales): the K loop below
+  // is unrolled by ST, so every access names its stage statically and the
+  // compiler can see that reading one stage does not wait on the loads
+  // filling another.  Stages past ST are placeholders.
+  constexpr int SA_B = BM * kBK, SB_B = BN * kBK;
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[ST > 2 ? SA_B : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[ST > 3 ? SA_B : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[ST > 2 ? SB_B : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[ST > 3 ? SB_B : 16];
+  __shared__ __attribute__((aligned(256))) float sS0[BM];
+  __shared__ __attribute__((aligned(256))) float sS1[BM];
+  __shared__ __attribute__((aligned(256))) float sS2[ST > 2 ? BM : 4];
+  __shared__ __attribute__((aligned(256))) float sS3[ST > 3 ? BM : 4];
+  uint8_t* const stA[4] = {sA0, sA1, sA2, sA3};
+  uint8_t* const stB[4] = {sB0, sB1, sB2, sB3};
+  float* const stS[4] = {sS0, sS1, sS2, sS3};
 
   // ---- which tile: grouped order over the tile list (see the XCD note above)
   const int n_tiles = N / BN;
@@ -214,26 +230,36 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + ((size_t)e_sel * N + n0) * K), (short)0, BN * K, 0x00020000);
 
-  // Row scales (K-block-major, so a tile's rows are contiguous) are loaded
-  // into registers one step ahead by the first BM threads and written to the
-  // stage's scale block at the end of the step; rows past the buffer are
-  // clamped and only feed rows that are never stored.  In LDS the scale of
-  // row wm*WM + i*16 + q sits at ((i/4) * (BM/WM) * 16 + wm*16 + q) * 4 +
-  // i%4, so a lane -- whose outputs all belong to row q of each of its MI
+  // Row scales (K-block-major, so the BM scales of a tile and k-block are
+  // contiguous) go to LDS with the tiles: each wave issues one 4-byte load
+  // per lane for 64 of the rows (waves past BM/64 repeat a block: identical
+  // values to identical places).  Lane p of block q fetches the row whose
+  // scale belongs at position 64 q + p: in LDS the scale of row
+  // wm*WM + i*16 + r sits at ((i/4) * (BM/WM) * 16 + wm*16 + r) * 4 + i%4,
+  // so a lane -- whose outputs all belong to row r of each of its MI
   // subtiles -- reads its MI scales as MI/4 float4s, and the 16 lanes of a
-  // read cover one contiguous 256-byte run.  The weight-block scale of this wave's
-  // columns is one wave-uniform value per step, read with a scalar load one
-  // step ahead.
+  // read cover one contiguous 256-byte run.  Rows past the buffer read
+  // another k-block's scales or zero and only feed rows that are never
+  // stored.  The weight-block scale of this wave's columns is one
+  // wave-uniform value per step, read with a scalar load one step ahead.
   const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * Kb;
-  const bool row_owner = tid < BM;
-  int sa_row = row0 + (row_owner ? tid : 0);
-  sa_row = sa_row < rows_total ? sa_row : rows_total - 1;
-  const int sa_pos =
-      ((((tid % WM) / 16) >> 2) * (BM / WM) * 16 + (tid / WM) * 16 + (tid & 15)) * 4 +
-      (((tid % WM) / 16) & 3);
+  const int sc_blk = wave % (BM / 64);
+  int sc_row;
+  {
+    const int p = sc_blk * 64 + lane;
+    const int t = p >> 2;
+    const int i = (t / (NWM * 16)) * 4 + (p & 3);
+    const int wq = t % (NWM * 16);
+    sc_row = (wq / 16) * WM + i * 16 + (wq & 15);
+  }
+  const long long sa_bytes = (long long)Kb * rows_total * 4;
+  const __amdgpu_buffer_rsrc_t rsrc_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)SA, (short)0, (int)(sa_bytes > 0x7ffff000LL ? 0x7ffff000LL : sa_bytes),
+      0x00020000);
 
-  // Every wave issues the same CH_PER_WAVE tile-chunk loads per stage.
-  auto issue = [&](int kb, uint8_t* stA, uint8_t* stB) {
+  // Every wave issues the same LPS loads per stage: CH_PER_WAVE tile chunks
+  // and one block of row scales.
+  auto issue = [&](int kb, uint8_t* tA, uint8_t* tB, float* tS) {
 #pragma unroll
     for (int u = 0; u < CH_PER_WAVE; ++u) {
       const int c = wave * CH_PER_WAVE + u;   // wave-uniform
@@ -241,15 +267,18 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       const uint32_t lo = (u & 1) ? lane_off1 : lane_off0;   // parity of c is u's
       if (c < A_CHUNKS) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc_a, (lds_void*)(stA + c * 1024), 16,
+            rsrc_a, (lds_void*)(tA + c * 1024), 16,
             (int)(lo + (uint32_t)(c * 8) * (uint32_t)K + kofs), 0, 0, 0);
       } else {
         const int cb = c - A_CHUNKS;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc_b, (lds_void*)(stB + cb * 1024), 16,
+            rsrc_b, (lds_void*)(tB + cb * 1024), 16,
             (int)(lo + (uint32_t)(cb * 8) * (uint32_t)K + kofs), 0, 0, 0);
       }
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc_s, (lds_void*)(tS + sc_blk * 64), 4,
+        (int)(((uint32_t)kb * (uint32_t)rows_total + (uint32_t)(row0 + sc_row)) * 4u), 0, 0, 0);
   };
 
 
@@ -264,16 +293,22 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int wcol = wn * WN;
   float sw_cur = 0.f;   // weight-block scale of the current step
 
-  // One K step on stage (tA, tB, tS).  The MFMAs compute the transposed
-  // product (weights as the first operand), so a lane's four outputs of a
-  // subtile are four consecutive columns of one row: one row scale per
-  // lane and subtile.  The B fragments and the lane's row scales are read
-  // first, then the loads of step kb + 1 are issued into the other stage
-  // (freed by the barrier ending the previous step) and stay in flight
-  // while the step's MFMAs run; the A fragments are read row by row as the
-  // MFMA pipeline needs them.
-  auto step = [&](int kb, const uint8_t* tA, const uint8_t* tB, const float* tS, uint8_t* nA,
-                  uint8_t* nB, float* nS) {
+  // One K step on stage S (which holds k-block kb).  First the loads of
+  // k-block kb + ST - 1 are issued into the stage the previous step used
+  // (freed by the barrier that ended it), so ST - 1 k-blocks are in flight
+  // while this one is multiplied.  The MFMAs compute the transposed product
+  // (weights as the first operand), so a lane's four outputs of a subtile
+  // are four consecutive columns of one row: one row scale per lane and
+  // subtile.  The B fragments and the lane's row scales are read first; the
+  // A fragments are read row by row as the MFMA pipeline needs them.
+  auto step = [&](int kb, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    constexpr int SF = (S + ST - 1) % ST;   // the stage freed by the previous step
+    const uint8_t* tA = stA[S];
+    const uint8_t* tB = stB[S];
+    const float* tS = stS[S];
+    const bool refill = kb + ST - 1 < Kb;
+    if (refill) issue(kb + ST - 1, stA[SF], stB[SF], stS[SF]);
     v8i bf[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
@@ -283,11 +318,6 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       const float4 v = *reinterpret_cast<const float4*>(
           &tS[((i4 >> 2) * (BM / WM) * 16 + wm * 16 + r16) * 4]);
       fs[i4] = v.x; fs[i4 + 1] = v.y; fs[i4 + 2] = v.z; fs[i4 + 3] = v.w;
-    }
-    float sa_next = 0.f;
-    if (kb + 1 < Kb) {
-      issue(kb + 1, nA, nB);
-      if (row_owner) sa_next = SA[(size_t)(kb + 1) * rows_total + sa_row];
     }
     const float sw = sw_cur;
     sw_cur = kb + 1 < Kb ? SWw[kb + 1] : 0.f;
@@ -344,20 +374,32 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
-    if (kb + 1 < Kb && row_owner) nS[sa_pos] = sa_next;
-    // the next stage must have landed for every wave before it is read
-    wait_vmcnt<0>();
+    // k-block kb + 1 must have landed for every wave before it is read; the
+    // ST - 2 newer k-blocks stay in flight (past the last refill, fewer loads
+    // are outstanding and all are waited for)
+    if (refill)
+      wait_vmcnt<(ST - 2) * LPS>();
+    else
+      wait_vmcnt<0>();
     lds_barrier();
   };
 
   sw_cur = SWw[0];
-  issue(0, sA0, sB0);
-  if (row_owner) sS0[sa_pos] = SA[sa_row];
-  wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < Kb) issue(s, stA[s], stB[s], stS[s]);
+  if (Kb >= ST - 1)
+    wait_vmcnt<(ST - 2) * LPS>();
+  else
+    wait_vmcnt<0>();
   lds_barrier();
-  for (int kb = 0; kb < Kb; kb += 2) {
-    step(kb, sA0, sB0, sS0, sA1, sB1, sS1);
-    if (kb + 1 < Kb) step(kb + 1, sA1, sB1, sS1, sA0, sB0, sS0);
+  for (int kb = 0; kb < Kb; kb += ST) {
+    step(kb, std::integral_constant<int, 0>());
+    if (kb + 1 < Kb) step(kb + 1, std::integral_constant<int, 1>());
+    if constexpr (ST > 2)
+      if (kb + 2 < Kb) step(kb + 2, std::integral_constant<int, 2>());
+    if constexpr (ST > 3)
+      if (kb + 3 < Kb) step(kb + 3, std::integral_constant<int, 3>());
   }
 
   // ---- epilogue: in subtile (i, j) a lane holds row r16 and columns
@@ -378,7 +420,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int kTag>
+template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
@@ -389,22 +431,22 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag>),
+  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, ST, kTag>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
                      offsets, counts, E, rows_total, N, K, c);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
-// Tile configurations (BM, BN, WM, WN, GM).  Large problems use 256 x 256
+// Tile configurations (BM, BN, WM, WN, GM, stages).  Large problems use 256 x 256
 // tiles (8 waves of 128 x 64, two per SIMD); problems too small to give
 // every CU two such tiles use 128 x 128 (4 waves of 64 x 64, two workgroups
 // per CU).  kTag keeps the gate/up (1) and down (2) projections as separate
 // kernel symbols so that profiles attribute time per projection.
 #ifndef MOE_GEMM_BIG
-#define MOE_GEMM_BIG 256, 256, 128, 64, 2
+#define MOE_GEMM_BIG 256, 256, 128, 64, 2, 2
 #endif
 #ifndef MOE_GEMM_SMALL
-#define MOE_GEMM_SMALL 128, 128, 64, 64, 4
+#define MOE_GEMM_SMALL 128, 128, 64, 64, 4, 2
 #endif
 
 }  // namespace moe
