@@ -105,6 +105,61 @@ def cpu_baseline(cfg, idx, w, n_tokens):
             "seconds": round(dt, 3), "rows_per_s": n_rows / dt}
 
 
+def bench_dense(args, M, N, K):
+    """Dense block-scaled FP8 GEMM: c[M, N] = A[M, K] W[N, K]^T with 1x128
+    activation and 128x128 weight scales.  Operands are seeded N(0, 1) and
+    N(0, 0.02) bf16 values quantised on the device."""
+    import numpy as np
+    import torch
+    import fp8_routed_expert_amd as fre
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xb = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+    wb = (torch.randn(N, K, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    a = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    sa_rows = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    w = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sw = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev)
+    fre.moe_quantize_fp8(xb, 1, a, sa_rows)
+    fre.moe_quantize_fp8(wb, 128, w, sw)
+    sa = sa_rows.t().contiguous()           # K-block-major
+    del xb, wb, sa_rows
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        fre.moe_gemm_fp8(a, sa, w, sw, c)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        fre.moe_gemm_fp8(a, sa, w, sw, c)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    flops = 2.0 * M * N * K
+    nbytes = M * K + M * (K // 128) * 4 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2
+    tf = flops / (kern_ms * 1e-3) / 1e12
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    mfma = flops / nbytes >= FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return {
+        "metric": "dense block-scaled FP8 GEMM TFLOP/s", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": f"dense gemm M={M} N={N} K={K}, 1x128 / 128x128 scales",
+                   "M": M, "N": N, "K": K},
+        "roofline": ({"kernel": "grouped_gemm_fp8 (dense)", "bound": "mfma",
+                      "achieved": round(tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None} if mfma else
+                     {"kernel": "grouped_gemm_fp8 (dense)", "bound": "hbm",
+                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +174,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB before every timed step "
                          "(outside the timed span) to evict the memory-side cache")
+    ap.add_argument("--dense", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
+                    help="time the dense FP8 GEMM (moe_gemm_fp8) at this shape instead "
+                         "of the layer")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first "
                          "(reference for scaling HBM byte counters)")
@@ -134,8 +192,11 @@ def main():
     import fp8_routed_expert_amd as fre
     from workloads import CONFIGS, routing, activations, weights
 
-    cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
+    if args.dense:
+        print(json.dumps(bench_dense(args, *args.dense)), flush=True)
+        return
+    cfg = CONFIGS[args.config]
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -3,7 +3,7 @@ parallelism.  The arithmetic lives in the HIP library libmoe_fp8.so (C ABI in
 include/moe_fp8.h); this package is its Python binding."""
 
 from .ops import (moe_layout_workspace_bytes, moe_dispatch_layout,  # noqa: F401
-                  moe_grouped_gemm_fp8, moe_act_requant, moe_combine,
+                  moe_grouped_gemm_fp8, moe_gemm_fp8, moe_act_requant, moe_combine,
                   moe_quantize_fp8, LAYOUT_CONTIGUOUS, LAYOUT_MASKED,
                   ERR_BAD_EXPERT, ERR_OVERFLOW, ERR_BAD_INDEX)
 from .layer import MoELayer, contiguous_rows  # noqa: F401

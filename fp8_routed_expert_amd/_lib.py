@@ -28,6 +28,8 @@ SIGNATURES = {
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int32, [
         _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_gemm_fp8": (ctypes.c_int32, [
+        _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_act_requant": (ctypes.c_int32, [
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "moe_combine": (ctypes.c_int32, [
@@ -36,7 +38,7 @@ SIGNATURES = {
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 

@@ -186,10 +186,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   float* const stS[4] = {sS0, sS1, sS2, sS3};
 
   // ---- which tile: grouped order over the tile list (see the XCD note above)
+  // kTag 3: dense product (one weight matrix, every row valid); the tile
+  // rows then follow from rows_total alone and offsets/counts are not read
+  constexpr bool kDense = kTag == 3;
   const int n_tiles = N / BN;
-  int e_sel, row0 = 0, row_end = 0;
-  const int total_m = find_mtile<BM>(offsets, counts, E, rows_total, 0x7fffffff, e_sel,
-                                     row0, row_end);
+  int e_sel = 0, row0 = 0, row_end = 0;
+  const int total_m =
+      kDense ? (rows_total + BM - 1) / BM
+             : find_mtile<BM>(offsets, counts, E, rows_total, 0x7fffffff, e_sel, row0, row_end);
   const int total = total_m * n_tiles;
   const int logical = blockIdx.x;
   if (logical >= total) return;
@@ -200,8 +204,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int gm_cnt = min(GM, total_m - gm0);
   const int tile_n = in_grp / gm_cnt;
   const int tile_m = gm0 + (in_grp - tile_n * gm_cnt);
-  find_mtile<BM>(offsets, counts, E, rows_total, tile_m, e_sel, row0, row_end);
-  if (e_sel < 0) return;
+  if (kDense) {
+    e_sel = 0;
+    row0 = tile_m * BM;
+    row_end = rows_total;
+  } else {
+    find_mtile<BM>(offsets, counts, E, rows_total, tile_m, e_sel, row0, row_end);
+    if (e_sel < 0) return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -426,7 +436,8 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
                            const int32_t* counts, int E, int rows_total, int N, int K,
                            uint16_t* c, hipStream_t st) {
   if (N % BN != 0) return MOE_UNSUPPORTED_SHAPE;
-  long long m_tiles = (long long)rows_total / BM + E;
+  long long m_tiles = kTag == 3 ? ((long long)rows_total + BM - 1) / BM
+                                : (long long)rows_total / BM + E;
   long long blocks = m_tiles * (N / BN);
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
@@ -440,8 +451,9 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 // Tile configurations (BM, BN, WM, WN, GM, stages).  Large problems use 256 x 256
 // tiles (8 waves of 128 x 64, two per SIMD); problems too small to give
 // every CU two such tiles use 128 x 128 (4 waves of 64 x 64, two workgroups
-// per CU).  kTag keeps the gate/up (1) and down (2) projections as separate
-// kernel symbols so that profiles attribute time per projection.
+// per CU).  kTag keeps the gate/up (1) and down (2) projections and the
+// dense product (3) as separate kernel symbols so that profiles attribute
+// time per projection.
 #ifndef MOE_GEMM_BIG
 #define MOE_GEMM_BIG 256, 256, 128, 64, 2, 2
 #endif
@@ -479,4 +491,21 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(
                                              rows_total, N, K, c, st)
                  : launch<MOE_GEMM_SMALL, 2>(a, a_scale, w, w_scale, offsets, counts, E,
                                              rows_total, N, K, c, st);
+}
+
+extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* w,
+                                     const float* w_scale, int M, int N, int K, uint16_t* c,
+                                     void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return MOE_INVALID_ARG;
+  if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
+  if (M == 0) return MOE_OK;
+  if (!a || !a_scale || !w || !w_scale || !c) return MOE_INVALID_ARG;
+  if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15) return MOE_UNSUPPORTED_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool big = N % 256 == 0 && (long long)(M / 256) * (N / 256) >= 512;
+  if (big)
+    return launch<MOE_GEMM_BIG, 3>(a, a_scale, w, w_scale, nullptr, nullptr, 1, M, N, K, c,
+                                   st);
+  return launch<MOE_GEMM_SMALL, 3>(a, a_scale, w, w_scale, nullptr, nullptr, 1, M, N, K, c,
+                                   st);
 }

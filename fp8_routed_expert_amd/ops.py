@@ -91,6 +91,19 @@ def moe_grouped_gemm_fp8(a, a_scale, w, w_scale, offsets, counts, c, status,
     check(st, "moe_grouped_gemm_fp8")
 
 
+def moe_gemm_fp8(a, a_scale, w, w_scale, c, stream=None):
+    """c = dense block-scaled FP8 product of a [M, K] with w [N, K]
+    (a_scale [K/128, M], w_scale [N/128, K/128])."""
+    M, K = a.shape
+    N = w.shape[0]
+    lib = load()
+    st = lib.moe_gemm_fp8(
+        _ptr(a, _U8, "a", (M, K)), _ptr(a_scale, _F32, "a_scale", (K // 128, M)),
+        _ptr(w, _U8, "w", (N, K)), _ptr(w_scale, _F32, "w_scale", (N // 128, K // 128)),
+        M, N, K, _ptr(c, _BF16, "c", (M, N)), _stream(stream))
+    check(st, "moe_gemm_fp8")
+
+
 def moe_act_requant(h, offsets, counts, q, q_scale, status, stream=None):
     """q, q_scale = E4M3 1x128 requantisation of silu(h[:, :I]) * h[:, I:]."""
     rows_total, I2 = h.shape

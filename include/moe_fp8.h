@@ -158,6 +158,28 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
                                   int32_t* status_dev, void* stream);
 
 /*
+ * moe_gemm_fp8 -- dense block-scaled FP8 product for the linears outside
+ * the MoE block [H100-EP DeepGEMM 集成: besides the grouped MoE GEMMs the
+ * library offers a general GEMM kernel for non-MoE operations].  For every
+ * m in [0, M), n in [0, N):
+ *
+ *   c[m, n] = bf16_rne( sum_kb  a_scale[kb, m] * w_scale[n/128, kb]
+ *                               * sum_{k in block kb} a[m, k] * w[n, k] )
+ *
+ * with the same arithmetic as moe_grouped_gemm_fp8 (it is that kernel with
+ * one weight matrix and every row valid).
+ *
+ *   a        [M, K] e4m3               a_scale [K/128, M] f32 (K-block-major)
+ *   w        [N, K] e4m3               w_scale [N/128, K/128] f32
+ *   c        [M, N] bf16
+ * N and K must be multiples of 128; M >= 0 is arbitrary (M = 0 launches
+ * nothing).  No device status word: the call has no data-dependent errors.
+ */
+moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale,
+                          const uint8_t* w, const float* w_scale, int M, int N,
+                          int K, uint16_t* c, void* stream);
+
+/*
  * moe_act_requant — SiLU(gate) * up, re-quantised to E4M3 with fresh 1x128
  * scales (reading: SiLU and the gate/up order are not on the pages).  For
  * every valid row m and j in [0, I):

@@ -54,6 +54,11 @@ def test_host_argument_errors_launch_nothing():
     # misaligned A -> UNSUPPORTED_SHAPE
     assert lib.moe_grouped_gemm_fp8(ctypes.c_void_p(4097), fake, fake, fake, fake, fake, 2,
                                     256, 128, 256, fake, fake, N) == 2
+    # dense GEMM: K not a multiple of 128, negative M, null scale, M = 0 is a no-op
+    assert lib.moe_gemm_fp8(fake, fake, fake, fake, 64, 128, 100, fake, N) == 2
+    assert lib.moe_gemm_fp8(fake, fake, fake, fake, -1, 128, 128, fake, N) == 1
+    assert lib.moe_gemm_fp8(fake, N, fake, fake, 64, 128, 128, fake, N) == 1
+    assert lib.moe_gemm_fp8(fake, fake, fake, fake, 0, 128, 128, fake, N) == 0
     # act: I not a multiple of 128
     assert lib.moe_act_requant(fake, fake, fake, 2, 16, 100, fake, fake, fake, N) == 2
     # combine: K too large / H not a multiple of 128
