@@ -252,7 +252,7 @@ def combine_rows(y_of_slot, slot_of, topk_w, tokens):
 # chained layer (optionally on a subset of source tokens)
 # --------------------------------------------------------------------------
 def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
-          align_m=BLOCK, rows=None, capacity=None, tokens=None):
+          align_m=BLOCK, rows=None, capacity=None, tokens=None, requant=None):
     """Run S1-S8 on the CPU.
 
     x [T, H] E4M3 codes, x_scale [T, H/128]; w13 [E, 2I, H], s13
@@ -264,8 +264,10 @@ def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
     Returns a dict: the layout, `slots` (the permuted rows computed), and for
     those rows `h` [n, 2I], `q2` [n, I], `q2_scale` [n, I/128], `y` [n, H]
     (float64 bf16 values / uint8 codes), plus `tokens` and `out`
-    [len(tokens), H].
+    [len(tokens), H].  `requant` replaces S6's quantiser (default
+    act_requant); it maps h to (codes, fp32 block scales).
     """
+    requant = act_requant if requant is None else requant
     E = w13.shape[0]
     T = x.shape[0]
     L = dispatch_layout(topk_idx, E, layout, align_m, rows, capacity)
@@ -286,7 +288,7 @@ def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
             continue
         xa, xs = x[src[sel]], x_scale[src[sel]]
         h[sel] = gemm_rows(xa, xs, w13[e], s13[e])
-        q, qs = act_requant(h[sel])
+        q, qs = requant(h[sel])
         q2[sel], q2s[sel] = q, qs
         y[sel] = gemm_rows(q, qs, w2[e], s2[e])
     pos = {int(s): i for i, s in enumerate(slots)}
