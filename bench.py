@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB before every timed step "
                          "(outside the timed span) to evict the memory-side cache")
+    ap.add_argument("--scales", choices=("fp32", "e8m0"), default="fp32",
+                    help="block-scale format: fp32 (default) or packed power-of-two "
+                         "exponents applied by the matrix cores")
     ap.add_argument("--dense", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
                     help="time the dense FP8 GEMM (moe_gemm_fp8) at this shape instead "
                          "of the layer")
@@ -215,19 +218,28 @@ def main():
 
     E, H, I, T, K = cfg.E, cfg.H, cfg.I, cfg.T, cfg.K
     x = torch.empty(T, H, dtype=torch.uint8, device=dev)
-    xs = torch.empty(T, H // 128, dtype=torch.float32, device=dev)
     w13 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=dev)
-    s13 = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
     w2 = torch.empty(E, H, I, dtype=torch.uint8, device=dev)
-    s2 = torch.empty(E, H // 128, I // 128, dtype=torch.float32, device=dev)
-    fre.moe_quantize_fp8(bf(xb), 1, x, xs)
-    fre.moe_quantize_fp8(bf(w13b), 128, w13, s13)
-    fre.moe_quantize_fp8(bf(w2b), 128, w2, s2)
+    if args.scales == "e8m0":
+        hw, iw = (H // 128 + 3) // 4, (I // 128 + 3) // 4
+        xs = torch.empty(T, hw, dtype=torch.int32, device=dev)
+        s13 = torch.empty(E, 2 * I // 128, hw, dtype=torch.int32, device=dev)
+        s2 = torch.empty(E, H // 128, iw, dtype=torch.int32, device=dev)
+        quant = fre.moe_quantize_fp8_e8m0
+    else:
+        xs = torch.empty(T, H // 128, dtype=torch.float32, device=dev)
+        s13 = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
+        s2 = torch.empty(E, H // 128, I // 128, dtype=torch.float32, device=dev)
+        quant = fre.moe_quantize_fp8
+    quant(bf(xb), 1, x, xs)
+    quant(bf(w13b), 128, w13, s13)
+    quant(bf(w2b), 128, w2, s2)
     del xb, w13b, w2b
     idx_d = torch.from_numpy(idx).to(dev)
     w_d = torch.from_numpy(w).to(dev)
     rows = cfg.capacity if cfg.layout == fre.LAYOUT_MASKED else fre.contiguous_rows(R, E, cfg.align_m)
-    layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev)
+    layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev,
+                         scale_fmt=args.scales)
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -314,7 +326,7 @@ def main():
     bytes_g2 = live * (H * I + hb * ib * 4) + R * (I + 4 * ib) + R * H * 2
     tflops = flops / (ms * 1e-3) / 1e12
     launch_key = f"{cfg.name}:R={R}:rows={rows}"
-    traffic = stored_traffic(launch_key)
+    traffic = stored_traffic(launch_key) if args.scales == "fp32" else None
     pct = lambda q: round(float(np.percentile(step_ms, q)), 4)
     result = {
         "metric": METRIC,
@@ -334,7 +346,7 @@ def main():
                                f"{'masked' if cfg.layout else 'contiguous'} layout",
                    "experts": E, "hidden": H, "intermediate": I, "tokens": T,
                    "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total,
-                   "experts_with_rows": live},
+                   "experts_with_rows": live, "block_scales": args.scales},
         "timing": {"mode": "hipgraph replay" if graph is not None else "eager launches",
                    "cache_flush_mib": args.flush_mib,
                    "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90)},
@@ -367,7 +379,7 @@ def main():
                                   "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.scales == "fp32":
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(cfg, idx, w, args.cpu_tokens)
     print(json.dumps(result), flush=True)

@@ -28,6 +28,15 @@ SIGNATURES = {
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int32, [
         _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_quantize_fp8_e8m0": (ctypes.c_int32, [
+        _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_dispatch_layout_e8m0": (ctypes.c_int32, [
+        _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
+    "moe_grouped_gemm_fp8_e8m0": (ctypes.c_int32, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_act_requant_e8m0": (ctypes.c_int32, [
+        _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "moe_gemm_fp8": (ctypes.c_int32, [
         _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_act_requant": (ctypes.c_int32, [
@@ -38,7 +47,7 @@ SIGNATURES = {
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 

@@ -51,10 +51,13 @@ __device__ __forceinline__ bool row_valid(const int32_t* offsets, const int32_t*
   return m >= s && m < en;
 }
 
+// kPow2: power-of-two scales stored as E8M0 bytes, four 128-column blocks
+// per 32-bit word, words K-block-major ([ceil(I/512), rows_total]).
+template <bool kPow2>
 __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int E, int rows_total, int I,
-    uint8_t* __restrict__ q, float* __restrict__ q_scale) {
+    uint8_t* __restrict__ q, void* __restrict__ q_scale) {
   const int m = blockIdx.x;
   const int j0 = blockIdx.y * kActCols + threadIdx.x * 8;
   const bool in_row = j0 < I;
@@ -77,6 +80,23 @@ __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
   }
   amax = group16_max(amax);   // all 16 lanes of a block share in_row
   if (!in_row) return;
+  if (kPow2) {
+    const int e = e8m0_exponent(amax);
+    const float inv = e8m0_inverse(e);
+    uint2 out;
+    out.x = pack2_e4m3(v[0] * inv, v[1] * inv) | (pack2_e4m3(v[2] * inv, v[3] * inv) << 16);
+    out.y = pack2_e4m3(v[4] * inv, v[5] * inv) | (pack2_e4m3(v[6] * inv, v[7] * inv) << 16);
+    *reinterpret_cast<uint2*>(q + (size_t)m * I + j0) = out;
+    if ((threadIdx.x & 15) == 0) {
+      const int jb = j0 / kBlock, ib = I / kBlock;
+      uint8_t* w = reinterpret_cast<uint8_t*>(q_scale) +
+                   ((size_t)(jb >> 2) * rows_total + m) * 4;
+      w[jb & 3] = (uint8_t)(e + 127);
+      if (jb == ib - 1)
+        for (int p = (jb & 3) + 1; p < 4; ++p) w[p] = 127;   // past the last block
+    }
+    return;
+  }
   const float sc = block_scale(amax);
   float qv[8];
   if (sc >= 0x1p-90f) {
@@ -91,18 +111,18 @@ __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
   out.x = pack2_e4m3(qv[0], qv[1]) | (pack2_e4m3(qv[2], qv[3]) << 16);
   out.y = pack2_e4m3(qv[4], qv[5]) | (pack2_e4m3(qv[6], qv[7]) << 16);
   *reinterpret_cast<uint2*>(q + (size_t)m * I + j0) = out;
-  if ((threadIdx.x & 15) == 0) q_scale[(size_t)(j0 / kBlock) * rows_total + m] = sc;
+  if ((threadIdx.x & 15) == 0)
+    reinterpret_cast<float*>(q_scale)[(size_t)(j0 / kBlock) * rows_total + m] = sc;
 }
 
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
-                                        const int32_t* counts, int E, int rows_total,
-                                        int I, uint8_t* q, float* q_scale,
-                                        int32_t* status_dev, void* stream) {
-  (void)status_dev;
+template <bool kPow2>
+static moe_status_t act_requant(const uint16_t* h, const int32_t* offsets,
+                                const int32_t* counts, int E, int rows_total, int I,
+                                uint8_t* q, void* q_scale, void* stream) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0) return MOE_INVALID_ARG;
   if (I % kBlock != 0) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts) return MOE_INVALID_ARG;
@@ -110,9 +130,25 @@ extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offset
   if (!h || !q || !q_scale) return MOE_INVALID_ARG;
   if (((uintptr_t)h | (uintptr_t)q) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(act_requant_kernel,
+  hipLaunchKernelGGL((act_requant_kernel<kPow2>),
                      dim3((unsigned)rows_total, (unsigned)((I + kActCols - 1) / kActCols)),
                      dim3(kActThreads), 0, st, h, offsets, counts, E, rows_total, I, q,
                      q_scale);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}
+
+extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
+                                        const int32_t* counts, int E, int rows_total,
+                                        int I, uint8_t* q, float* q_scale,
+                                        int32_t* status_dev, void* stream) {
+  (void)status_dev;
+  return act_requant<false>(h, offsets, counts, E, rows_total, I, q, q_scale, stream);
+}
+
+extern "C" moe_status_t moe_act_requant_e8m0(const uint16_t* h, const int32_t* offsets,
+                                             const int32_t* counts, int E, int rows_total,
+                                             int I, uint8_t* q, uint32_t* q_scale,
+                                             int32_t* status_dev, void* stream) {
+  (void)status_dev;
+  return act_requant<true>(h, offsets, counts, E, rows_total, I, q, q_scale, stream);
 }

@@ -59,6 +59,26 @@ __device__ __forceinline__ float group16_max(float v) {
   return v;
 }
 
+// Power-of-two block scale (E8M0): the exponent e of the smallest power of
+// two not below fp32(amax / 448), from the bits of that correctly rounded
+// quotient: 1.M x 2^(E-127) needs E - 127 when M == 0 and E - 126
+// otherwise; a subnormal quotient M x 2^-149 needs -126 above 2^-127 and
+// is clamped to the E8M0 minimum -127 at or below it.  An all-zero block
+// takes e = 0 (scale 1).
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t b = __float_as_uint(amax / kE4M3Max);
+  const uint32_t E = (b >> 23) & 0xffu, M = b & 0x7fffffu;
+  if (E == 0) return M > (1u << 22) ? -126 : -127;
+  return (int)E - (M == 0 ? 127 : 126);
+}
+
+// 2^-e as an fp32 value (exact for e in [-127, 127]).
+__device__ __forceinline__ float e8m0_inverse(int e) {
+  return e >= 127 ? __uint_as_float(0x00400000u)          // 2^-127 (subnormal)
+                  : __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
 // Block scale for a 128-wide block with absolute maximum amax (>= 0).
 __device__ __forceinline__ float block_scale(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;

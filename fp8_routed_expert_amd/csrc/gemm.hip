@@ -137,7 +137,7 @@ __device__ __forceinline__ int find_mtile(const int32_t* offsets, const int32_t*
   return acc;
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag>
+template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag, bool kPow2>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
@@ -252,7 +252,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // another k-block's scales or zero and only feed rows that are never
   // stored.  The weight-block scale of this wave's columns is one
   // wave-uniform value per step, read with a scalar load one step ahead.
-  const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * Kb;
+  // kPow2: scales are E8M0 bytes packed four k-blocks per 32-bit word
+  // (row scales [ceil(Kb/4), rows_total] words, weight scales
+  // [E, N/128, ceil(Kb/4)] words); the MFMA applies them itself.
+  const int Kw = (Kb + 3) / 4;
+  const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * (kPow2 ? Kw : Kb);
   const int sc_blk = wave % (BM / 64);
   int sc_row;
   {
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     const int wq = t % (NWM * 16);
     sc_row = (wq / 16) * WM + i * 16 + (wq & 15);
   }
-  const long long sa_bytes = (long long)Kb * rows_total * 4;
+  const long long sa_bytes = (long long)(kPow2 ? Kw : Kb) * rows_total * 4;
   const __amdgpu_buffer_rsrc_t rsrc_s = __builtin_amdgcn_make_buffer_rsrc(
       (void*)SA, (short)0, (int)(sa_bytes > 0x7ffff000LL ? 0x7ffff000LL : sa_bytes),
       0x00020000);
@@ -288,7 +292,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc_s, (lds_void*)(tS + sc_blk * 64), 4,
-        (int)(((uint32_t)kb * (uint32_t)rows_total + (uint32_t)(row0 + sc_row)) * 4u), 0, 0, 0);
+        (int)(((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total +
+               (uint32_t)(row0 + sc_row)) * 4u), 0, 0, 0);
   };
 
 
@@ -330,7 +335,28 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       fs[i4] = v.x; fs[i4 + 1] = v.y; fs[i4 + 2] = v.z; fs[i4 + 3] = v.w;
     }
     const float sw = sw_cur;
-    sw_cur = kb + 1 < Kb ? SWw[kb + 1] : 0.f;
+    sw_cur = kb + 1 < Kb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+    if constexpr (kPow2) {
+      // E8M0 exponents of this k-block: the wave's weight block (uniform)
+      // and each lane's row in every subtile row i
+      const int sh = 8 * (kb & 3);
+      const int sw_e = (int)((__float_as_uint(sw) >> sh) & 0xffu);
+      int sa_e[MI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sa_e[i] = (int)((__float_as_uint(fs[i]) >> sh) & 0xffu);
+      // the hardware applies 2^(sw_e - 127) to the weight operand and
+      // 2^(sa_e - 127) to the row operand and accumulates into acc
+      v8i af_next = load_frag(tA, wm * WM + r16, g);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const v8i af = af_next;
+        if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bf[j], af, acc[i][j], 0, 0, 0, sw_e, 0, sa_e[i]);
+      }
+    } else {
     // two-deep software pipeline over the wave's MFMA rows: the MFMAs of
     // row i are issued while the FMAs promote row i-1 (whose products are
     // complete), so matrix-core and VALU work overlap and only two sets of
@@ -377,6 +403,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
     // keep the promotions of this step ahead of the barrier (otherwise they
     // are sunk into the next step, where they no longer overlap the MFMAs)
@@ -430,7 +457,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag>
+template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag, bool kPow2 = false>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
@@ -442,7 +469,7 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, ST, kTag>),
+  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, ST, kTag, kPow2>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
                      offsets, counts, E, rows_total, N, K, c);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
@@ -465,12 +492,11 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 
 using namespace moe;
 
-extern "C" moe_status_t moe_grouped_gemm_fp8(
-    const uint8_t* a, const float* a_scale, const uint8_t* w,
-    const float* w_scale, const int32_t* offsets, const int32_t* counts, int E,
-    int rows_total, int N, int K, uint16_t* c, int32_t* status_dev,
-    void* stream) {
-  (void)status_dev;
+template <bool kPow2>
+static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w,
+                                 const float* w_scale, const int32_t* offsets,
+                                 const int32_t* counts, int E, int rows_total, int N, int K,
+                                 uint16_t* c, void* stream) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || N <= 0 || K <= 0)
     return MOE_INVALID_ARG;
   if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
@@ -483,14 +509,34 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(
   // host-known sizes only, so the choice is the same inside graph capture
   const bool big = N % 256 == 0 && (long long)(rows_total / 256) * (N / 256) >= 512;
   if (big)
-    return gate_up ? launch<MOE_GEMM_BIG, 1>(a, a_scale, w, w_scale, offsets, counts, E,
-                                             rows_total, N, K, c, st)
-                   : launch<MOE_GEMM_BIG, 2>(a, a_scale, w, w_scale, offsets, counts, E,
-                                             rows_total, N, K, c, st);
-  return gate_up ? launch<MOE_GEMM_SMALL, 1>(a, a_scale, w, w_scale, offsets, counts, E,
-                                             rows_total, N, K, c, st)
-                 : launch<MOE_GEMM_SMALL, 2>(a, a_scale, w, w_scale, offsets, counts, E,
-                                             rows_total, N, K, c, st);
+    return gate_up ? launch<MOE_GEMM_BIG, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st)
+                   : launch<MOE_GEMM_BIG, 2, kPow2>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st);
+  return gate_up ? launch<MOE_GEMM_SMALL, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st)
+                 : launch<MOE_GEMM_SMALL, 2, kPow2>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st);
+}
+
+extern "C" moe_status_t moe_grouped_gemm_fp8(
+    const uint8_t* a, const float* a_scale, const uint8_t* w,
+    const float* w_scale, const int32_t* offsets, const int32_t* counts, int E,
+    int rows_total, int N, int K, uint16_t* c, int32_t* status_dev,
+    void* stream) {
+  (void)status_dev;
+  return grouped_gemm<false>(a, a_scale, w, w_scale, offsets, counts, E, rows_total, N, K, c,
+                             stream);
+}
+
+extern "C" moe_status_t moe_grouped_gemm_fp8_e8m0(
+    const uint8_t* a, const uint32_t* a_scale, const uint8_t* w, const uint32_t* w_scale,
+    const int32_t* offsets, const int32_t* counts, int E, int rows_total, int N, int K,
+    uint16_t* c, int32_t* status_dev, void* stream) {
+  (void)status_dev;
+  return grouped_gemm<true>(a, reinterpret_cast<const float*>(a_scale), w,
+                            reinterpret_cast<const float*>(w_scale), offsets, counts, E,
+                            rows_total, N, K, c, stream);
 }
 
 extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* w,

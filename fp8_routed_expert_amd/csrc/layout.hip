@@ -276,16 +276,17 @@ __global__ __launch_bounds__(256) void permute_rows(
 }
 
 // Scales in the permuted, K-block-major layout: a_scale[kb, slot] =
-// x_scale[row_src[slot], kb].  A workgroup takes 64 consecutive slots and
+// x_scale[row_src[slot], kb], moved as 4-byte words (an fp32 scale, or four
+// packed E8M0 exponents; hb is the number of words per source row).  A workgroup takes 64 consecutive slots and
 // transposes through LDS: each wave reads whole source scale rows (64
 // consecutive block scales of one token) and writes 64 consecutive slots of
 // one block column, so both sides are contiguous runs.
 constexpr int kScTile = 64;
 
 __global__ __launch_bounds__(256) void permute_scales(
-    const float* __restrict__ x_scale, const int32_t* __restrict__ row_src, int T, int hb,
-    int rows_total, float* __restrict__ a_scale) {
-  __shared__ float tile[64][kScTile + 1];
+    const uint32_t* __restrict__ x_scale, const int32_t* __restrict__ row_src, int T, int hb,
+    int rows_total, uint32_t* __restrict__ a_scale) {
+  __shared__ uint32_t tile[64][kScTile + 1];
   __shared__ int src_of[kScTile];
   const int slot0 = blockIdx.x * kScTile;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -342,11 +343,13 @@ extern "C" size_t moe_layout_workspace_bytes(int T, int K, int E) {
   return (size_t)(2 * nc * E) * sizeof(int32_t);
 }
 
-extern "C" moe_status_t moe_dispatch_layout(
-    const int32_t* topk_idx, const uint8_t* x, const float* x_scale, int T,
-    int K, int E, int H, int layout, int align_m, int rows, int32_t* counts,
+// hw = 4-byte scale words per source row (H/128 fp32 scales, or H/512
+// rounded up of packed E8M0 words).
+static moe_status_t dispatch(
+    const int32_t* topk_idx, const uint8_t* x, const uint32_t* x_scale, int T,
+    int K, int E, int H, int hw, int layout, int align_m, int rows, int32_t* counts,
     int32_t* offsets, int32_t* slot_of, int32_t* row_src, int32_t* row_expert,
-    uint8_t* a, float* a_scale, void* workspace, size_t workspace_bytes,
+    uint8_t* a, uint32_t* a_scale, void* workspace, size_t workspace_bytes,
     int32_t* status_dev, void* stream) {
   if (T < 0 || K <= 0 || K > MOE_MAX_TOPK || E <= 0 || E > MOE_MAX_EXPERTS ||
       H <= 0 || rows < 0)
@@ -394,8 +397,28 @@ extern "C" moe_status_t moe_dispatch_layout(
     hipLaunchKernelGGL(permute_rows, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, x,
                        slot_of, T, K, H, pieces, plen, (int)rows_total, a);
     hipLaunchKernelGGL(permute_scales, dim3((unsigned)((rows_total + kScTile - 1) / kScTile)),
-                       dim3(256), 0, st, x_scale, row_src, T, H / kBlock, (int)rows_total,
-                       a_scale);
+                       dim3(256), 0, st, x_scale, row_src, T, hw, (int)rows_total, a_scale);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}
+
+extern "C" moe_status_t moe_dispatch_layout(
+    const int32_t* topk_idx, const uint8_t* x, const float* x_scale, int T, int K, int E,
+    int H, int layout, int align_m, int rows, int32_t* counts, int32_t* offsets,
+    int32_t* slot_of, int32_t* row_src, int32_t* row_expert, uint8_t* a, float* a_scale,
+    void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream) {
+  return dispatch(topk_idx, x, reinterpret_cast<const uint32_t*>(x_scale), T, K, E, H,
+                  H / kBlock, layout, align_m, rows, counts, offsets, slot_of, row_src,
+                  row_expert, a, reinterpret_cast<uint32_t*>(a_scale), workspace,
+                  workspace_bytes, status_dev, stream);
+}
+
+extern "C" moe_status_t moe_dispatch_layout_e8m0(
+    const int32_t* topk_idx, const uint8_t* x, const uint32_t* x_scale, int T, int K, int E,
+    int H, int layout, int align_m, int rows, int32_t* counts, int32_t* offsets,
+    int32_t* slot_of, int32_t* row_src, int32_t* row_expert, uint8_t* a, uint32_t* a_scale,
+    void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream) {
+  return dispatch(topk_idx, x, x_scale, T, K, E, H, (H / kBlock + 3) / 4, layout, align_m,
+                  rows, counts, offsets, slot_of, row_src, row_expert, a, a_scale, workspace,
+                  workspace_bytes, status_dev, stream);
 }

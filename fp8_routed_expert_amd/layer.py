@@ -9,6 +9,10 @@ the five library calls of one layer on a stream:
 All arithmetic happens in the HIP library; this class only holds memory.
 The call sequence allocates nothing and reads nothing back, so it can be
 captured into a hipGraph (torch.cuda.CUDAGraph) and replayed.
+
+scale_fmt "fp32" keeps fp32 block scales; "e8m0" uses packed power-of-two
+scales (int32 words of four biased exponents; the *_e8m0 calls), in which
+case x_scale and the weight scales passed in must be packed the same way.
 """
 
 import torch
@@ -22,8 +26,12 @@ def contiguous_rows(R, E, align_m=128):
 
 
 class MoELayer:
-    def __init__(self, E, H, I, T, K, layout, rows, align_m=128, device="cuda"):
+    def __init__(self, E, H, I, T, K, layout, rows, align_m=128, device="cuda",
+                 scale_fmt="fp32"):
         """rows: M_cap for the contiguous layout, capacity C for masked."""
+        if scale_fmt not in ("fp32", "e8m0"):
+            raise ValueError(f"scale_fmt {scale_fmt!r}")
+        self.scale_fmt = scale_fmt
         self.E, self.H, self.I, self.T, self.K = E, H, I, T, K
         self.layout, self.rows, self.align_m = layout, rows, align_m
         self.rows_total = E * rows if layout == ops.LAYOUT_MASKED else rows
@@ -35,10 +43,14 @@ class MoELayer:
         self.row_src = torch.zeros(R, **i32)
         self.row_expert = torch.zeros(R, **i32)
         self.a = torch.zeros(R, H, dtype=torch.uint8, device=d)
-        self.a_scale = torch.zeros(H // 128, R, dtype=torch.float32, device=d)
+        pk = scale_fmt == "e8m0"
+        sdt = torch.int32 if pk else torch.float32
+        self.a_scale = torch.zeros((H // 128 + 3) // 4 if pk else H // 128, R, dtype=sdt,
+                                   device=d)
         self.h = torch.zeros(R, 2 * I, dtype=torch.bfloat16, device=d)
         self.q2 = torch.zeros(R, I, dtype=torch.uint8, device=d)
-        self.q2_scale = torch.zeros(I // 128, R, dtype=torch.float32, device=d)
+        self.q2_scale = torch.zeros((I // 128 + 3) // 4 if pk else I // 128, R, dtype=sdt,
+                                    device=d)
         self.y = torch.zeros(R, H, dtype=torch.bfloat16, device=d)
         self.out = torch.zeros(T, H, dtype=torch.bfloat16, device=d)
         self.workspace = torch.zeros(max(1, ops.moe_layout_workspace_bytes(T, K, E)),
@@ -46,22 +58,28 @@ class MoELayer:
         self.status = torch.zeros(1, **i32)
 
     def dispatch(self, topk_idx, x, x_scale, stream=None):
-        ops.moe_dispatch_layout(topk_idx, x, x_scale, self.E, self.layout, self.align_m,
-                                self.rows, self.counts, self.offsets, self.slot_of,
-                                self.row_src, self.row_expert, self.a, self.a_scale,
-                                self.workspace, self.status, stream)
+        f = (ops.moe_dispatch_layout_e8m0 if self.scale_fmt == "e8m0"
+             else ops.moe_dispatch_layout)
+        f(topk_idx, x, x_scale, self.E, self.layout, self.align_m, self.rows, self.counts,
+          self.offsets, self.slot_of, self.row_src, self.row_expert, self.a, self.a_scale,
+          self.workspace, self.status, stream)
 
     def gemm1(self, w13, s13, stream=None):
-        ops.moe_grouped_gemm_fp8(self.a, self.a_scale, w13, s13, self.offsets, self.counts,
-                                 self.h, self.status, stream)
+        self._gemm(self.a, self.a_scale, w13, s13, self.offsets, self.counts, self.h,
+                   self.status, stream)
+
+    def _gemm(self, *args):
+        f = (ops.moe_grouped_gemm_fp8_e8m0 if self.scale_fmt == "e8m0"
+             else ops.moe_grouped_gemm_fp8)
+        f(*args)
 
     def act(self, stream=None):
-        ops.moe_act_requant(self.h, self.offsets, self.counts, self.q2, self.q2_scale,
-                            self.status, stream)
+        f = ops.moe_act_requant_e8m0 if self.scale_fmt == "e8m0" else ops.moe_act_requant
+        f(self.h, self.offsets, self.counts, self.q2, self.q2_scale, self.status, stream)
 
     def gemm2(self, w2, s2, stream=None):
-        ops.moe_grouped_gemm_fp8(self.q2, self.q2_scale, w2, s2, self.offsets, self.counts,
-                                 self.y, self.status, stream)
+        self._gemm(self.q2, self.q2_scale, w2, s2, self.offsets, self.counts, self.y,
+                   self.status, stream)
 
     def combine(self, topk_w, stream=None):
         ops.moe_combine(self.y, self.slot_of, topk_w, self.out, self.status, stream)

@@ -146,3 +146,83 @@ def moe_quantize_fp8(x, block_rows, q, scale, stream=None):
         _ptr(x, _BF16 + _F32, "x"), 1 if is_f32 else 0, rows, cols, block_rows,
         _ptr(q, _U8, "q"), _ptr(scale, _F32, "scale"), _stream(stream))
     check(st, "moe_quantize_fp8")
+
+
+# ---- packed power-of-two (E8M0) scales: four 128-wide blocks per 32-bit
+# word, held in int32 tensors; see moe_fp8.h for the layouts.
+def _words(nb):
+    return (nb + 3) // 4
+
+
+def moe_quantize_fp8_e8m0(x, block_rows, q, scale, stream=None):
+    """moe_quantize_fp8 with packed E8M0 scales: scale int32
+    [rows / block_rows, ceil(cols / 512)]."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    is_f32 = x.dtype == torch.float32
+    if q.numel() != x.numel() or scale.numel() != rows // block_rows * _words(cols // 128):
+        raise ValueError("moe_quantize_fp8_e8m0: q / scale sizes do not match x")
+    lib = load()
+    st = lib.moe_quantize_fp8_e8m0(
+        _ptr(x, _BF16 + _F32, "x"), 1 if is_f32 else 0, rows, cols, block_rows,
+        _ptr(q, _U8, "q"), _ptr(scale, _I32, "scale"), _stream(stream))
+    check(st, "moe_quantize_fp8_e8m0")
+
+
+def moe_dispatch_layout_e8m0(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
+                             offsets, slot_of, row_src, row_expert, a, a_scale,
+                             workspace, status, stream=None):
+    """moe_dispatch_layout with packed scales: x_scale int32 [T, ceil(H/512)],
+    a_scale int32 [ceil(H/512), rows_total]."""
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    hw = _words(H // 128)
+    rows_total = E * rows if layout == LAYOUT_MASKED else rows
+    lib = load()
+    st = lib.moe_dispatch_layout_e8m0(
+        _ptr(topk_idx, _I32, "topk_idx", (T, K)), _ptr(x, _U8, "x", (T, H)),
+        _ptr(x_scale, _I32, "x_scale", (T, hw)), T, K, E, H, layout,
+        align_m, rows, _ptr(counts, _I32, "counts", (E,)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)),
+        _ptr(slot_of, _I32, "slot_of", (T, K)),
+        _ptr(row_src, _I32, "row_src", (rows_total,)),
+        _ptr(row_expert, _I32, "row_expert", (rows_total,)),
+        _ptr(a, _U8, "a", (rows_total, H)),
+        _ptr(a_scale, _I32, "a_scale", (hw, rows_total)),
+        _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_dispatch_layout_e8m0")
+
+
+def moe_grouped_gemm_fp8_e8m0(a, a_scale, w, w_scale, offsets, counts, c, status,
+                              stream=None):
+    """moe_grouped_gemm_fp8 with packed scales: a_scale int32
+    [ceil(K/512), rows_total], w_scale int32 [E, N/128, ceil(K/512)]."""
+    E, N, K = w.shape
+    rows_total = a.shape[0]
+    kw = _words(K // 128)
+    lib = load()
+    st = lib.moe_grouped_gemm_fp8_e8m0(
+        _ptr(a, _U8, "a", (rows_total, K)),
+        _ptr(a_scale, _I32, "a_scale", (kw, rows_total)),
+        _ptr(w, _U8, "w", (E, N, K)),
+        _ptr(w_scale, _I32, "w_scale", (E, N // 128, kw)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)), _ptr(counts, _I32, "counts", (E,)),
+        E, rows_total, N, K, _ptr(c, _BF16, "c", (rows_total, N)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_grouped_gemm_fp8_e8m0")
+
+
+def moe_act_requant_e8m0(h, offsets, counts, q, q_scale, status, stream=None):
+    """moe_act_requant with packed scales: q_scale int32 [ceil(I/512), rows_total]."""
+    rows_total, I2 = h.shape
+    I = I2 // 2
+    E = counts.numel()
+    lib = load()
+    st = lib.moe_act_requant_e8m0(
+        _ptr(h, _BF16, "h"), _ptr(offsets, _I32, "offsets", (E + 1,)),
+        _ptr(counts, _I32, "counts", (E,)), E, rows_total, I,
+        _ptr(q, _U8, "q", (rows_total, I)),
+        _ptr(q_scale, _I32, "q_scale", (_words(I // 128), rows_total)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_act_requant_e8m0")

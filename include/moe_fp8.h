@@ -234,6 +234,51 @@ moe_status_t moe_quantize_fp8(const void* x, int x_is_f32, int rows, int cols,
                               int block_rows, uint8_t* q, float* scale,
                               void* stream);
 
+/*
+ * Packed power-of-two scales (E8M0) [GB200 方法实现细节: the FP8 GEMM API
+ * quantises and packs the input scales].  Reading: a block's scale is the
+ * smallest power of two not below fp32(amax / 448) (1 for an all-zero
+ * block, 2^-127 when the quotient underflows), so q = e4m3_rne(v / s) is
+ * exact scaling; the scale is stored as its biased exponent byte e + 127,
+ * four consecutive 128-wide blocks along K per little-endian 32-bit word
+ * (byte j of word w holds block 4w + j; bytes past a row's last block are
+ * 127).  The matrix cores apply these scales themselves
+ * (v_mfma_scale_f32_16x16x128_f8f6f4), with no fp32 promotion step.  Each
+ * call below is its fp32-scale counterpart above with these scale arrays:
+ *   moe_quantize_fp8_e8m0     scale: block_rows 1 -> [rows, ceil(cols/512)]
+ *                             words (row-major per row, as dispatched with
+ *                             the token); block_rows 128 -> [rows/128,
+ *                             ceil(cols/512)]
+ *   moe_dispatch_layout_e8m0  x_scale [T, ceil(H/512)] words ->
+ *                             a_scale [ceil(H/512), rows_total] words
+ *                             (K-word-major)
+ *   moe_grouped_gemm_fp8_e8m0 a_scale [ceil(K/512), rows_total] words,
+ *                             w_scale [E, N/128, ceil(K/512)] words;
+ *                             c = bf16_rne(sum_kb 2^(ea + ew) * block product)
+ *   moe_act_requant_e8m0      q_scale [ceil(I/512), rows_total] words
+ * Argument checks, status bits and layouts otherwise as above.
+ */
+moe_status_t moe_quantize_fp8_e8m0(const void* x, int x_is_f32, int rows,
+                                   int cols, int block_rows, uint8_t* q,
+                                   uint32_t* scale, void* stream);
+moe_status_t moe_dispatch_layout_e8m0(
+    const int32_t* topk_idx, const uint8_t* x, const uint32_t* x_scale, int T,
+    int K, int E, int H, int layout, int align_m, int rows, int32_t* counts,
+    int32_t* offsets, int32_t* slot_of, int32_t* row_src, int32_t* row_expert,
+    uint8_t* a, uint32_t* a_scale, void* workspace, size_t workspace_bytes,
+    int32_t* status_dev, void* stream);
+moe_status_t moe_grouped_gemm_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
+                                       const uint8_t* w, const uint32_t* w_scale,
+                                       const int32_t* offsets,
+                                       const int32_t* counts, int E,
+                                       int rows_total, int N, int K,
+                                       uint16_t* c, int32_t* status_dev,
+                                       void* stream);
+moe_status_t moe_act_requant_e8m0(const uint16_t* h, const int32_t* offsets,
+                                  const int32_t* counts, int E, int rows_total,
+                                  int I, uint8_t* q, uint32_t* q_scale,
+                                  int32_t* status_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from oracle import moe
+from oracle import moe, e8m0
 from workloads import CONFIGS, routing, activations, weights, bf16_to_f32
 
 _THREADS = min(16, os.cpu_count() or 1)
@@ -67,3 +67,41 @@ def rows_for(cfg, idx):
         return cfg.capacity
     R = int((idx >= 0).sum())
     return R + cfg.E * (cfg.align_m - 1)
+
+
+def _quant_expert_e8m0(cfg, e):
+    w13b, w2b = weights(cfg, experts=[e])
+    q13, e13 = e8m0.quantize_blocks(bf16_to_f32(w13b[0]), 128)
+    q2, e2 = e8m0.quantize_blocks(bf16_to_f32(w2b[0]), 128)
+    return q13, e13, q2, e2
+
+
+def as_words(p):
+    """uint32 packed words as the int32 array the device tensors hold."""
+    return np.ascontiguousarray(np.asarray(p, np.uint32).view(np.int32))
+
+
+@functools.lru_cache(maxsize=2)
+def layer_inputs_e8m0(cid, experts_needed_only=False):
+    """layer_inputs with power-of-two scales (oracle.e8m0): for x, W13 and W2
+    the codes, the exponents, the packed int32 words the device takes
+    (xp [T, ceil(H/512)], p13 [E, 2I/128, ceil(H/512)], p2 [E, H/128,
+    ceil(I/512)]) and the fp32 scale values 2^e the oracle takes."""
+    cfg = CONFIGS[cid]
+    idx, w = routing(cfg)
+    x, xe = e8m0.quantize_blocks(bf16_to_f32(activations(cfg)), 1)
+    E, I, H = cfg.E, cfg.I, cfg.H
+    w13 = np.zeros((E, 2 * I, H), np.uint8)
+    e13 = np.zeros((E, 2 * I // 128, H // 128), np.int32)
+    w2 = np.zeros((E, H, I), np.uint8)
+    e2 = np.zeros((E, H // 128, I // 128), np.int32)
+    used = np.unique(idx[idx >= 0])
+    experts = used if experts_needed_only else range(E)
+
+    def qe(e):
+        w13[e], e13[e], w2[e], e2[e] = _quant_expert_e8m0(cfg, e)
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(qe, experts))
+    return dict(cfg=cfg, idx=idx, w=w, x=x, xe=xe, xs=e8m0.scales(xe), xp=as_words(e8m0.pack(xe)),
+                w13=w13, e13=e13, s13=e8m0.scales(e13), p13=as_words(e8m0.pack(e13)),
+                w2=w2, e2=e2, s2=e8m0.scales(e2), p2=as_words(e8m0.pack(e2)))

@@ -36,14 +36,16 @@ def _operands(g, M, N, K):
 
 def test_dense_exact_integers_pow2_scales(gpu):
     """Small-integer codes and power-of-two scales keep every sum exact, so
-    the result must equal the oracle's bit for bit; M is ragged (not a
-    multiple of any tile) so the last tile is partly outside the matrix."""
+    the result must equal the oracle's bit for bit (codes in [-4, 4], scales
+    2^[-2, 2]: every partial sum is a multiple of 2^-4 below 2^17, exact in
+    fp32 in any order); M is ragged (not a multiple of any tile) so the last
+    tile is partly outside the matrix."""
     g = np.random.default_rng(41)
     M, N, K = 300, 384, 512
     a = e4m3_encode(g.integers(-4, 5, (M, K)).astype(np.float64))
     w = e4m3_encode(g.integers(-4, 5, (N, K)).astype(np.float64))
-    sa = np.ldexp(1.0, g.integers(-4, 5, (M, K // 128))).astype(np.float32)
-    sw = np.ldexp(1.0, g.integers(-4, 5, (N // 128, K // 128))).astype(np.float32)
+    sa = np.ldexp(1.0, g.integers(-2, 3, (M, K // 128))).astype(np.float32)
+    sw = np.ldexp(1.0, g.integers(-2, 3, (N // 128, K // 128))).astype(np.float32)
     got = _run_dense(a, sa, w, sw)
     ref = moe.gemm_rows(a, sa, w, sw)
     assert np.array_equal(bf16_decode(got), ref)
