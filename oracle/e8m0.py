@@ -8,13 +8,13 @@ rest of the layer (layout, GEMM definition, SiLU, combine) is oracle.moe
 unchanged, fed with the scales below.
 
 Readings (listed again in the design notes):
-  R12 a block's scale is the smallest power of two not below
+  R18 a block's scale is the smallest power of two not below
       fp32(amax / 448): s = 2^e, e = ceil(log2(fp32(amax / 448))); e = 0
       when amax == 0; e is kept in the E8M0 range [-127, 127] (a quotient
       that underflows to zero for amax > 0 takes the smallest, -127).
-  R13 codes are E4M3_RNE(v / s) with v = fp32(value).  Dividing by a power
+  R19 codes are E4M3_RNE(v / s) with v = fp32(value).  Dividing by a power
       of two is exact and |v / s| <= 448, so no saturation occurs.
-  R14 packing: a scale is stored as its biased exponent byte e + 127
+  R20 packing: a scale is stored as its biased exponent byte e + 127
       (E8M0), four consecutive 128-wide blocks along K per 32-bit word,
       little-endian (byte j of word w belongs to block 4w + j); the bytes
       past the last block of a row are 127 (scale 1).
@@ -29,7 +29,7 @@ E8M0_BIAS = 127
 
 
 def scale_exponents(amax):
-    """R12: e = ceil(log2(fp32(amax / 448))), 0 for amax == 0, clipped to
+    """R18: e = ceil(log2(fp32(amax / 448))), 0 for amax == 0, clipped to
     [-127, 127] (-127 when the quotient underflows to zero).  With fp32(amax / 448) = m * 2^x, m in [0.5, 1) (frexp),
     the ceiling is x - 1 when m == 0.5 (an exact power of two) and x
     otherwise."""
@@ -43,7 +43,7 @@ def scale_exponents(amax):
 
 
 def quantize_blocks(values, block_rows):
-    """R12-R13 on a 2-D array in blocks of block_rows x 128.  Returns
+    """R18-R19 on a 2-D array in blocks of block_rows x 128.  Returns
     (codes uint8 [R, C], exponents int32 [R / block_rows, C / 128])."""
     v = np.asarray(values).astype(np.float32)
     R, C = v.shape
@@ -60,7 +60,7 @@ def scales(e):
 
 
 def pack(e):
-    """R14: exponents [..., nb] -> uint32 words [..., ceil(nb / 4)]."""
+    """R20: exponents [..., nb] -> uint32 words [..., ceil(nb / 4)]."""
     e = np.asarray(e, dtype=np.int64)
     nb = e.shape[-1]
     nw = (nb + 3) // 4
@@ -79,7 +79,7 @@ def unpack(words, nb):
 
 
 def act_requant(h):
-    """S6 with R12-R13: SiLU(gate) * up re-quantised in 1x128 blocks.
+    """S6 with R18-R19: SiLU(gate) * up re-quantised in 1x128 blocks.
     Returns (codes [M, I], fp32 scales 2^e [M, I/128]) for oracle.moe.layer."""
     q, e = quantize_blocks(silu_mul(h), 1)
     return q, scales(e)
