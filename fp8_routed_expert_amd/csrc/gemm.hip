@@ -64,6 +64,7 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
@@ -439,21 +440,58 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       if (kb + 3 < Kb) step(kb + 3, std::integral_constant<int, 3>());
   }
 
-  // ---- epilogue: in subtile (i, j) a lane holds row r16 and columns
-  // 4g .. 4g+3: four bf16 values, one 8-byte store
+  // ---- epilogue.  In subtile (i, j) a lane holds row r16 and columns
+  // 4g .. 4g+3.  Stored directly, every store instruction would write 16
+  // scattered 32-byte pieces; instead each wave stages its WM x WN bf16
+  // sub-tile (rows of WN * 2 = 128 bytes) in a region of its own in the
+  // stage memory -- free now: the last step waited for every load and ended
+  // with a barrier -- and stores it back as 16-byte pieces, eight lanes per
+  // contiguous 128-byte row.  Only the wave's own LDS accesses are ordered,
+  // so no workgroup barrier is needed.  The 8-byte chunks of staged row r
+  // are XOR-permuted by 2 * ((r >> 1) & 7), which keeps the chunk pairs of
+  // a 16-byte read together.  The output is written with non-temporal
+  // stores.  Measured at the prefill shape: GEMM2 -5%, GEMM1 -4% against
+  // direct 8-byte stores.
+  constexpr int kRegion = WM * WN * 2;
+  constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
+  static_assert(WN * 2 == 128, "staged rows are 128 bytes");
+  static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 2 * (kPerA + kPerB), "staging space");
+  uint8_t* region;
+  {
+    int w = wave;
+    if (w < kPerA) {
+      region = sA0 + w * kRegion;
+    } else if ((w -= kPerA) < kPerA) {
+      region = sA1 + w * kRegion;
+    } else if ((w -= kPerA) < kPerB) {
+      region = sB0 + w * kRegion;
+    } else {
+      region = sB1 + (w - kPerB) * kRegion;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int row = row0 + wm * WM + i * 16 + r16;
-    if (row < row_end) {
-      uint16_t* crow = C + (size_t)row * N + n0 + wcol + 4 * g;
+    const int r = i * 16 + r16;
+    const int f = ((r >> 1) & 7) << 1;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        uint2 o;
-        o.x = f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
-        o.y = f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(crow + j * 16) = o;
-      }
+    for (int j = 0; j < NJ; ++j) {
+      uint2 o;
+      o.x = f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+      o.y = f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+      *reinterpret_cast<uint2*>(region + r * 128 + (((j * 4 + g) ^ f) << 3)) = o;
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int c16 = lane & 7;
+#pragma unroll
+  for (int rr = 0; rr < WM; rr += 8) {
+    const int r = rr + (lane >> 3);
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(region + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
+    const int row = row0 + wm * WM + r;
+    if (row < row_end)   // streamed out: not kept in the caches the tiles share
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                  reinterpret_cast<u32x4*>(C + (size_t)row * N + n0 + wcol + c16 * 8));
   }
 }
 
