@@ -11,8 +11,8 @@
 //
 // Design (gfx950):
 //   * Large problems: a workgroup computes a 256 x 256 tile of c with 8 waves
-//     of 128 x 64 (two waves per SIMD, one workgroup per CU, two 64 KB LDS
-//     stages).  Small problems: 128 x 128 tiles of 4 waves of 64 x 64, two
+//     of 128 x 64 (two waves per SIMD, one workgroup per CU, the full 160 KB
+//     of LDS).  Small problems: 128 x 128 tiles of 4 waves of 64 x 64, two
 //     workgroups per CU.  A wave's sub-tile is a grid of 16 x 16 MFMA
 //     subtiles.
 //   * K advances one 128-wide scale block per step.  v_mfma_f32_16x16x128
@@ -26,22 +26,28 @@
 //     promote the same column of row i - 1 (whose product is complete), so
 //     one wave overlaps its own matrix-core and VALU work; the accumulators
 //     stay in VGPRs.
-//   * A and B tiles (rows x 128 bytes) and the tile's row scales go from
-//     global memory straight into LDS with buffer_load ... lds (no staging
-//     registers), ST stages deep (ST - 1 k-blocks in flight while one is
-//     multiplied; both tile configurations use ST = 2: three and four
-//     stages, with one workgroup per CU, measured slower).  Each stage is
-//     its own LDS object and the K loop is unrolled by ST, so the compiler
-//     can see that reading one stage never waits on the loads filling
-//     another; the step barrier orders LDS only and the loads are waited for
-//     explicitly with vmcnt.  Inside every 16-row
-//     group the 16-byte chunks are XOR-permuted by (row & 7) ^ ((row >> 3) & 1)
-//     -- chosen through the per-lane global offset, since each load
-//     instruction fills 1 KB of LDS contiguously -- which measured free of
-//     bank conflicts for the fragment reads (4 LDS cycles per 1 KB read);
-//     the (row >> 1) & 7 permutation measured a 2-way conflict.
-//   * Row scales are K-block-major (contiguous per block); the weight-block
-//     scale of a wave's columns is a scalar load one step ahead.
+//   * A and B tiles (rows x 128 bytes) go from global memory straight into
+//     LDS with buffer_load ... lds (no staging registers).  A has three
+//     stages (its k-block kb + 2 is loaded while kb is multiplied), B two
+//     (kb + 1); at a 256 x 256 tile that is exactly the 160 KB of LDS.  The
+//     third A stage took 2-3% off the prefill gate/up GEMM and 7-20% off the
+//     decode ones; a third B stage instead measured slower at prefill.  The
+//     row scales (K-block-major, so contiguous per block) go straight to
+//     registers one step ahead; the weight-block scale of a wave's columns
+//     is a scalar load one step ahead.  Each stage is its own LDS object
+//     and the K loop is unrolled by 6, so every access names its stage
+//     statically.  The tile and scale loads are issued as inline assembly:
+//     the compiler then inserts no waits of its own for them (its
+//     conservative tracking of LDS-DMA targets otherwise waited for every
+//     load before the next fragment read, serialising the pipeline); they
+//     are waited for explicitly with vmcnt, which counts vector-memory
+//     operations in issue order, and the step barrier orders LDS only.
+//     Inside every 16-row group the 16-byte chunks are XOR-permuted by
+//     (row & 7) ^ ((row >> 3) & 1) -- chosen through the per-lane global
+//     offset, since each load instruction fills 1 KB of LDS contiguously --
+//     which measured free of bank conflicts for the fragment reads (4 LDS
+//     cycles per 1 KB read); the (row >> 1) & 7 permutation measured a 2-way
+//     conflict.
 //   * Tiles come from device-side offsets/counts: m-tiles are numbered
 //     expert by expert (ceil(valid rows / BM) per expert), so the grid is
 //     fixed by the buffer size alone and workgroups past the last real tile
@@ -75,17 +81,52 @@ constexpr int kXcds = 8;
 // makes every wave wait for all its outstanding vector loads -- including
 // the tile loads meant to stay in flight across the barrier.  Here the wave
 // waits for its own LDS reads (lgkmcnt) and meets the others; completion of
-// the tile loads is waited for explicitly with wait_vmcnt<n>() before it.
+// the tile loads is waited for explicitly with wait_loads<n>() before it.
 // Both are compiler memory barriers (asm with a memory clobber), so no
 // memory access is moved across them.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+typedef int v4i __attribute__((ext_vector_type(4)));
+// Raw buffer descriptor: base, stride 0, num_records bytes (offsets at or
+// past it read as zero), 32-bit data format.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  v4i r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)((b >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  return r;
+}
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane
+// (one wave instruction fills 1 KB).  M0 holds the LDS address; nothing else
+// in these kernels reads M0 (gfx9 LDS instructions do not use it), so the
+// clobber is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(v4i rsrc, uint8_t* lds, uint32_t voff) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;   // LDS byte offset
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(r) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (they complete in issue order), and publish the registers of
+// the asynchronous register loads issued before them (see load_scales).
+template <int N, int M>
+__device__ __forceinline__ void wait_loads(float (&r)[M]) {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#pragma unroll
+  for (int i = 0; i < M; ++i) asm volatile("" : "+v"(r[i]));
 }
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
@@ -146,7 +187,7 @@ __device__ __forceinline__ int find_mtile(const int32_t* offsets, const int32_t*
   return acc;
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag, bool kPow2>
+template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
@@ -155,48 +196,31 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   constexpr int NWM = BM / WM;
   constexpr int NWN = BN / WN;
   constexpr int NW = NWM * NWN;
-  constexpr int NT = 64 * NW;
   constexpr int MI = WM / 16;
   constexpr int NJ = WN / 16;
-  constexpr int NBW = (BN + kBlock - 1) / kBlock;   // weight-scale blocks per tile
   constexpr int A_CHUNKS = BM / 8;                   // 1 KB LDS chunks per stage
   constexpr int B_CHUNKS = BN / 8;
-  constexpr int CH_PER_WAVE = (A_CHUNKS + B_CHUNKS) / NW;
-  constexpr int LPS = CH_PER_WAVE + 1;   // loads per wave and step: tile chunks + row scales
-  static_assert((A_CHUNKS + B_CHUNKS) % NW == 0, "chunks must split evenly");
+  constexpr int CA = A_CHUNKS / NW;                  // A / B chunks per wave and stage
+  constexpr int CB = B_CHUNKS / NW;
+  static_assert(A_CHUNKS % NW == 0 && B_CHUNKS % NW == 0, "chunks must split evenly");
+  static_assert(CA % 2 == 0 && CB % 2 == 0, "chunk parity is static");
   static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
   static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
-  static_assert(BM % 64 == 0 && BM / 64 <= NW, "one scale load of 64 rows per wave");
-  static_assert(MI % 4 == 0, "row scales are read four at a time");
-  static_assert(CH_PER_WAVE % 2 == 0 && A_CHUNKS % 2 == 0, "chunk parity is static");
-  static_assert(ST >= 2 && ST <= 4, "pipeline depth");
-  static_assert((ST - 2) * LPS < 64, "vmcnt range");
+  static_assert(CA < 64, "vmcnt range");
   (void)kTag;
 
-  // One LDS object per stage (A rows, B rows, row scales): the K loop below
-  // is unrolled by ST, so every access names its stage statically and the
-  // compiler can see that reading one stage does not wait on the loads
-  // filling another.  Stages past ST are placeholders.
+  // A rows: three stages (k-blocks kb, kb + 1 landed or landing, kb + 2
+  // in flight); B rows: two stages.  Each stage is its own LDS object.
   constexpr int SA_B = BM * kBK, SB_B = BN * kBK;
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA_B];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA_B];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA2[ST > 2 ? SA_B : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA3[ST > 3 ? SA_B : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[SA_B];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB_B];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB_B];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB2[ST > 2 ? SB_B : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB3[ST > 3 ? SB_B : 16];
-  __shared__ __attribute__((aligned(256))) float sS0[BM];
-  __shared__ __attribute__((aligned(256))) float sS1[BM];
-  __shared__ __attribute__((aligned(256))) float sS2[ST > 2 ? BM : 4];
-  __shared__ __attribute__((aligned(256))) float sS3[ST > 3 ? BM : 4];
-  uint8_t* const stA[4] = {sA0, sA1, sA2, sA3};
-  uint8_t* const stB[4] = {sB0, sB1, sB2, sB3};
-  float* const stS[4] = {sS0, sS1, sS2, sS3};
+  uint8_t* const stA[3] = {sA0, sA1, sA2};
+  uint8_t* const stB[2] = {sB0, sB1};
 
   // ---- which tile: grouped order over the tile list (see the XCD note above)
-  // kTag 3: dense product (one weight matrix, every row valid); the tile
-  // rows then follow from rows_total alone and offsets/counts are not read
   constexpr bool kDense = kTag == 3;
   const int n_tiles = N / BN;
   int e_sel = 0, row0 = 0, row_end = 0;
@@ -231,130 +255,100 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int nb_w = N / kBlock;
   const int n0 = tile_n * BN;
 
-  // ---- direct-to-LDS tile loads through buffer descriptors.  LDS chunk c
-  // (1 KB = 8 rows x 128 B) is filled by one wave instruction: lane p writes
-  // bytes [16p, 16p+16) = row 8c + p/8, physical chunk p%8, which holds the
-  // logical 16-byte chunk (p%8) ^ (p/8) of that row.  The per-lane offset
-  // (row, chunk and K position) is bounds-checked against the descriptor, so
-  // rows past the end of the buffer read as zero and are never stored.
-  // Chunk c holds rows 8c + p/8 with p/8 < 8, so swz() of the row depends on
-  // the parity of c only: one lane offset per parity.
   const uint32_t lane_row = (uint32_t)(lane >> 3) * (uint32_t)K;
   const uint32_t lane_off0 = lane_row + (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4);
   const uint32_t lane_off1 = lane_row + (uint32_t)(((lane & 7) ^ swz(8 + (lane >> 3))) << 4);
   const long long a_bytes = (long long)(rows_total - row0) * K;
-  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (size_t)row0 * K), (short)0,
-      (int)(a_bytes > 0x7ffff000LL ? 0x7ffff000LL : a_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + ((size_t)e_sel * N + n0) * K), (short)0, BN * K, 0x00020000);
+  const v4i rsrc_a = make_rsrc(A + (size_t)row0 * K,
+                               (uint32_t)(a_bytes > 0x7ffff000LL ? 0x7ffff000LL : a_bytes));
+  const v4i rsrc_b = make_rsrc(W + ((size_t)e_sel * N + n0) * K, (uint32_t)(BN * K));
 
-  // Row scales (K-block-major, so the BM scales of a tile and k-block are
-  // contiguous) go to LDS with the tiles: each wave issues one 4-byte load
-  // per lane for 64 of the rows (waves past BM/64 repeat a block: identical
-  // values to identical places).  Lane p of block q fetches the row whose
-  // scale belongs at position 64 q + p: in LDS the scale of row
-  // wm*WM + i*16 + r sits at ((i/4) * (BM/WM) * 16 + wm*16 + r) * 4 + i%4,
-  // so a lane -- whose outputs all belong to row r of each of its MI
-  // subtiles -- reads its MI scales as MI/4 float4s, and the 16 lanes of a
-  // read cover one contiguous 256-byte run.  Rows past the buffer read
-  // another k-block's scales or zero and only feed rows that are never
-  // stored.  The weight-block scale of this wave's columns is one
-  // wave-uniform value per step, read with a scalar load one step ahead.
-  // kPow2: scales are E8M0 bytes packed four k-blocks per 32-bit word
-  // (row scales [ceil(Kb/4), rows_total] words, weight scales
-  // [E, N/128, ceil(Kb/4)] words); the MFMA applies them itself.
+  // Row scales go straight to registers: lane (g, r) needs the scale of row
+  // wm*WM + i*16 + r for each subtile row i, loaded one step ahead into
+  // fs_next.  Rows past the buffer read another k-block's scales or zero and
+  // only feed rows that are never stored.  kPow2: scales are E8M0 bytes
+  // packed four k-blocks per 32-bit word (row scales [ceil(Kb/4),
+  // rows_total] words, weight scales [E, N/128, ceil(Kb/4)] words); the
+  // MFMA applies them itself.
   const int Kw = (Kb + 3) / 4;
   const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * (kPow2 ? Kw : Kb);
-  const int sc_blk = wave % (BM / 64);
-  int sc_row;
-  {
-    const int p = sc_blk * 64 + lane;
-    const int t = p >> 2;
-    const int i = (t / (NWM * 16)) * 4 + (p & 3);
-    const int wq = t % (NWM * 16);
-    sc_row = (wq / 16) * WM + i * 16 + (wq & 15);
-  }
   const long long sa_bytes = (long long)(kPow2 ? Kw : Kb) * rows_total * 4;
-  const __amdgpu_buffer_rsrc_t rsrc_s = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)SA, (short)0, (int)(sa_bytes > 0x7ffff000LL ? 0x7ffff000LL : sa_bytes),
-      0x00020000);
-
-  // Every wave issues the same LPS loads per stage: CH_PER_WAVE tile chunks
-  // and one block of row scales.
-  auto issue = [&](int kb, uint8_t* tA, uint8_t* tB, float* tS) {
+  const v4i rsrc_s = make_rsrc(SA, (uint32_t)(sa_bytes > 0x7ffff000LL ? 0x7ffff000LL : sa_bytes));
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int wcol = wn * WN;
+  const uint32_t srow = (uint32_t)(row0 + wm * WM + r16);
+  float fs_next[MI];
 #pragma unroll
-    for (int u = 0; u < CH_PER_WAVE; ++u) {
-      const int c = wave * CH_PER_WAVE + u;   // wave-uniform
-      const uint32_t kofs = (uint32_t)kb * kBK;
-      const uint32_t lo = (u & 1) ? lane_off1 : lane_off0;   // parity of c is u's
-      if (c < A_CHUNKS) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc_a, (lds_void*)(tA + c * 1024), 16,
-            (int)(lo + (uint32_t)(c * 8) * (uint32_t)K + kofs), 0, 0, 0);
-      } else {
-        const int cb = c - A_CHUNKS;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc_b, (lds_void*)(tB + cb * 1024), 16,
-            (int)(lo + (uint32_t)(cb * 8) * (uint32_t)K + kofs), 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc_s, (lds_void*)(tS + sc_blk * 64), 4,
-        (int)(((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total +
-               (uint32_t)(row0 + sc_row)) * 4u), 0, 0, 0);
+  for (int i = 0; i < MI; ++i) fs_next[i] = 0.f;
+  // The loads are inline assembly, like the tile loads: a register is
+  // filled when its load completes, not when the instruction issues, so
+  // fs_next is read only after the wait_loads() that covers these loads,
+  // which is also where the compiler sees the values being written.
+  auto load_scales = [&](int kb) {
+    const uint32_t base = ((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total + srow) * 4u;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3"
+                   : "=v"(fs_next[i]) : "v"(base), "s"(rsrc_s), "n"(i * 64) : "memory");
   };
-
+  auto issue_a = [&](int kb, uint8_t* tA) {
+    const uint32_t kofs = (uint32_t)kb * kBK;
+#pragma unroll
+    for (int u = 0; u < CA; ++u) {
+      const int c = wave * CA + u;   // wave-uniform; parity of c is u's
+      dma16(rsrc_a, tA + c * 1024,
+            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K + kofs);
+    }
+  };
+  auto issue_b = [&](int kb, uint8_t* tB) {
+    const uint32_t kofs = (uint32_t)kb * kBK;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = wave * CB + u;
+      dma16(rsrc_b, tB + c * 1024,
+            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K + kofs);
+    }
+  };
 
   v4f acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  const int g = lane >> 4;
-  const int r16 = lane & 15;
-  const int wcol = wn * WN;
   float sw_cur = 0.f;   // weight-block scale of the current step
 
-  // One K step on stage S (which holds k-block kb).  First the loads of
-  // k-block kb + ST - 1 are issued into the stage the previous step used
-  // (freed by the barrier that ended it), so ST - 1 k-blocks are in flight
-  // while this one is multiplied.  The MFMAs compute the transposed product
-  // (weights as the first operand), so a lane's four outputs of a subtile
-  // are four consecutive columns of one row: one row scale per lane and
-  // subtile.  The B fragments and the lane's row scales are read first; the
-  // A fragments are read row by row as the MFMA pipeline needs them.
-  auto step = [&](int kb, auto stage) {
-    constexpr int S = decltype(stage)::value;
-    constexpr int SF = (S + ST - 1) % ST;   // the stage freed by the previous step
-    const uint8_t* tA = stA[S];
-    const uint8_t* tB = stB[S];
-    const float* tS = stS[S];
-    const bool refill = kb + ST - 1 < Kb;
-    if (refill) issue(kb + ST - 1, stA[SF], stB[SF], stS[SF]);
+  // One K step: A k-block kb in A stage SAi = kb % 3, B in B stage
+  // SBi = kb % 2.  At its start the B rows and row scales of k-block kb + 1
+  // and the A rows of k-block kb + 2 are issued (into stages freed by the
+  // barrier that ended the previous step); at its end only the A rows of
+  // kb + 2 may still be in flight.
+  auto step = [&](int kb, auto sa_i, auto sb_i) {
+    constexpr int SAi = decltype(sa_i)::value;
+    constexpr int SBi = decltype(sb_i)::value;
+    const uint8_t* tA = stA[SAi];
+    const uint8_t* tB = stB[SBi];
+    float fs[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) fs[i] = fs_next[i];
+    const bool rb = kb + 1 < Kb;
+    const bool ra = kb + 2 < Kb;
+    if (rb) {
+      issue_b(kb + 1, stB[(SBi + 1) % 2]);
+      load_scales(kb + 1);
+    }
+    if (ra) issue_a(kb + 2, stA[(SAi + 2) % 3]);
     v8i bf[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
-    float fs[MI];
-#pragma unroll
-    for (int i4 = 0; i4 < MI; i4 += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(
-          &tS[((i4 >> 2) * (BM / WM) * 16 + wm * 16 + r16) * 4]);
-      fs[i4] = v.x; fs[i4 + 1] = v.y; fs[i4 + 2] = v.z; fs[i4 + 3] = v.w;
-    }
     const float sw = sw_cur;
-    sw_cur = kb + 1 < Kb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+    sw_cur = rb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
     if constexpr (kPow2) {
-      // E8M0 exponents of this k-block: the wave's weight block (uniform)
-      // and each lane's row in every subtile row i
       const int sh = 8 * (kb & 3);
       const int sw_e = (int)((__float_as_uint(sw) >> sh) & 0xffu);
       int sa_e[MI];
 #pragma unroll
       for (int i = 0; i < MI; ++i) sa_e[i] = (int)((__float_as_uint(fs[i]) >> sh) & 0xffu);
-      // the hardware applies 2^(sw_e - 127) to the weight operand and
-      // 2^(sa_e - 127) to the row operand and accumulates into acc
       v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -366,11 +360,6 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
               bf[j], af, acc[i][j], 0, 0, 0, sw_e, 0, sa_e[i]);
       }
     } else {
-    // two-deep software pipeline over the wave's MFMA rows: the MFMAs of
-    // row i are issued while the FMAs promote row i-1 (whose products are
-    // complete), so matrix-core and VALU work overlap and only two sets of
-    // raw products are live.
-    // The A fragment of row i + 1 is read while row i is multiplied.
     v4f tprev[NJ];
     float fprev = 0.f;
     v8i af_next = load_frag(tA, wm * WM + r16, g);
@@ -399,10 +388,6 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
         for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
         fprev = fcur;
       }
-      // issue order inside the row: the next A fragment's LDS reads, then
-      // each MFMA of row i followed by the four FMAs that promote the same
-      // column of row i - 1 (left to itself the scheduler puts the FMAs
-      // first, where they wait for the MFMAs issued just before them)
       if (i > 0 && i < MI) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -414,38 +399,38 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       __builtin_amdgcn_sched_barrier(0);
     }
     }
-    // keep the promotions of this step ahead of the barrier (otherwise they
-    // are sunk into the next step, where they no longer overlap the MFMAs)
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
-    // k-block kb + 1 must have landed for every wave before it is read; the
-    // ST - 2 newer k-blocks stay in flight (past the last refill, fewer loads
-    // are outstanding and all are waited for)
-    if (refill)
-      wait_vmcnt<(ST - 2) * LPS>();
+    if (ra)
+      wait_loads<CA>(fs_next);
     else
-      wait_vmcnt<0>();
+      wait_loads<0>(fs_next);
     lds_barrier();
   };
 
   sw_cur = SWw[0];
-#pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < Kb) issue(s, stA[s], stB[s], stS[s]);
-  if (Kb >= ST - 1)
-    wait_vmcnt<(ST - 2) * LPS>();
-  else
-    wait_vmcnt<0>();
+  issue_b(0, sB0);
+  load_scales(0);
+  issue_a(0, sA0);
+  if (Kb > 1) {
+    issue_a(1, sA1);
+    wait_loads<CA>(fs_next);
+  } else {
+    wait_loads<0>(fs_next);
+  }
   lds_barrier();
-  for (int kb = 0; kb < Kb; kb += ST) {
-    step(kb, std::integral_constant<int, 0>());
-    if (kb + 1 < Kb) step(kb + 1, std::integral_constant<int, 1>());
-    if constexpr (ST > 2)
-      if (kb + 2 < Kb) step(kb + 2, std::integral_constant<int, 2>());
-    if constexpr (ST > 3)
-      if (kb + 3 < Kb) step(kb + 3, std::integral_constant<int, 3>());
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int kb = 0; kb < Kb; kb += 6) {
+    step(kb, I0(), I0());
+    if (kb + 1 < Kb) step(kb + 1, I1(), I1());
+    if (kb + 2 < Kb) step(kb + 2, I2(), I0());
+    if (kb + 3 < Kb) step(kb + 3, I0(), I1());
+    if (kb + 4 < Kb) step(kb + 4, I1(), I0());
+    if (kb + 5 < Kb) step(kb + 5, I2(), I1());
   }
 
   // ---- epilogue.  In subtile (i, j) a lane holds row r16 and columns
@@ -465,7 +450,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   constexpr int kRegion = WM * WN * 2;
   constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
   static_assert(WN * 2 == 128, "staged rows are 128 bytes");
-  static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 2 * (kPerA + kPerB), "staging space");
+  static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 3 * kPerA + 2 * kPerB, "staging space");
   uint8_t* region;
   {
     int w = wave;
@@ -473,6 +458,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       region = sA0 + w * kRegion;
     } else if ((w -= kPerA) < kPerA) {
       region = sA1 + w * kRegion;
+    } else if ((w -= kPerA) < kPerA) {
+      region = sA2 + w * kRegion;
     } else if ((w -= kPerA) < kPerB) {
       region = sB0 + w * kRegion;
     } else {
@@ -505,7 +492,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int ST, int kTag, bool kPow2 = false>
+template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2 = false>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
@@ -517,23 +504,23 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, ST, kTag, kPow2>),
+  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag, kPow2>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
                      offsets, counts, E, rows_total, N, K, c);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
-// Tile configurations (BM, BN, WM, WN, GM, stages).  Large problems use 256 x 256
+// Tile configurations (BM, BN, WM, WN, GM).  Large problems use 256 x 256
 // tiles (8 waves of 128 x 64, two per SIMD); problems too small to give
 // every CU two such tiles use 128 x 128 (4 waves of 64 x 64, two workgroups
 // per CU).  kTag keeps the gate/up (1) and down (2) projections and the
 // dense product (3) as separate kernel symbols so that profiles attribute
 // time per projection.
 #ifndef MOE_GEMM_BIG
-#define MOE_GEMM_BIG 256, 256, 128, 64, 2, 2
+#define MOE_GEMM_BIG 256, 256, 128, 64, 2
 #endif
 #ifndef MOE_GEMM_SMALL
-#define MOE_GEMM_SMALL 128, 128, 64, 64, 4, 2
+#define MOE_GEMM_SMALL 128, 128, 64, 64, 4
 #endif
 
 }  // namespace moe
