@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE-layer FP8 TFLOP/s + % of MFMA peak; routed token-rows/s per GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_ep32_prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_act_ep32_prefill_traffic.json")
 GEMM_SRC = os.path.join(ROOT, "fp8_routed_expert_amd", "csrc", "gemm.hip")
 
 
@@ -47,8 +47,9 @@ def gemm_source_hash():
 
 
 def stored_traffic(launch_key):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 --pmc summary,
-    or None when that summary is absent or was taken on another kernel."""
+    """HBM bytes per launch of the fused gate/up + activation kernel from the
+    committed rocprofv3 --pmc summary, or None when that summary is absent or
+    was taken on another kernel or workload."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -180,6 +181,9 @@ def main():
     ap.add_argument("--dense", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
                     help="time the dense FP8 GEMM (moe_gemm_fp8) at this shape instead "
                          "of the layer")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the gate/up GEMM and the activation as two calls "
+                         "(default: the layer's choice, fused at prefill sizes)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first "
                          "(reference for scaling HBM byte counters)")
@@ -239,27 +243,27 @@ def main():
     w_d = torch.from_numpy(w).to(dev)
     rows = cfg.capacity if cfg.layout == fre.LAYOUT_MASKED else fre.contiguous_rows(R, E, cfg.align_m)
     layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev,
-                         scale_fmt=args.scales)
+                         scale_fmt=args.scales, fuse_act=False if args.unfused else "auto")
+    fused = layer.fuse_act
     torch.cuda.synchronize()
+
+    if fused:
+        names = ["dispatch_layout", "gemm1_gate_up_act", "gemm2_down", "combine"]
+        stages = [lambda: layer.dispatch(idx_d, x, xs), lambda: layer.gemm1_act(w13, s13),
+                  lambda: layer.gemm2(w2, s2), lambda: layer.combine(w_d)]
+    else:
+        names = ["dispatch_layout", "gemm1_gate_up", "act_requant", "gemm2_down", "combine"]
+        stages = [lambda: layer.dispatch(idx_d, x, xs), lambda: layer.gemm1(w13, s13),
+                  lambda: layer.act(), lambda: layer.gemm2(w2, s2), lambda: layer.combine(w_d)]
+    n_ev = len(stages) + 1
 
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        layer.dispatch(idx_d, x, xs)
-        if evs is not None:
-            evs[1].record()
-        layer.gemm1(w13, s13)
-        if evs is not None:
-            evs[2].record()
-        layer.act()
-        if evs is not None:
-            evs[3].record()
-        layer.gemm2(w2, s2)
-        if evs is not None:
-            evs[4].record()
-        layer.combine(w_d)
-        if evs is not None:
-            evs[5].record()
+        for i, f in enumerate(stages):
+            f()
+            if evs is not None:
+                evs[i + 1].record()
 
     graph = None
     if args.graph:
@@ -294,7 +298,8 @@ def main():
     scratch = None
     if args.flush_mib:
         scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -303,11 +308,10 @@ def main():
         run_step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    step_ms = [events[k][0].elapsed_time(events[k][5]) for k in range(args.steps)]
+    step_ms = [events[k][0].elapsed_time(events[k][n_ev - 1]) for k in range(args.steps)]
     # wall clock over exactly K steps, unless flushes sit between them: then
     # the sum of the steps' own event spans
     ms = (t1 - t0) * 1e3 / args.steps if scratch is None else float(np.mean(step_ms))
-    names = ["dispatch_layout", "gemm1_gate_up", "act_requant", "gemm2_down", "combine"]
     per = None
     if graph is None:
         per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
@@ -322,11 +326,14 @@ def main():
     bytes_comb = R * 2 * H + T * 2 * H + T * K * 8
     # GEMM bytes: weights (and scales) of experts with rows, A and its scales, C
     live = int(np.count_nonzero(np.bincount(idx[idx >= 0], minlength=E)))
-    bytes_g1 = live * (2 * I * H + (2 * I // 128) * hb * 4) + R * (H + 4 * hb) + R * 2 * I * 2
+    # gate/up: writes h (bf16), or with the activation fused q2 and its scales
+    bytes_g1 = (live * (2 * I * H + (2 * I // 128) * hb * 4) + R * (H + 4 * hb) +
+                (R * (I + 4 * ib) if fused else R * 2 * I * 2))
     bytes_g2 = live * (H * I + hb * ib * 4) + R * (I + 4 * ib) + R * H * 2
     tflops = flops / (ms * 1e-3) / 1e12
     launch_key = f"{cfg.name}:R={R}:rows={rows}"
-    traffic = stored_traffic(launch_key) if args.scales == "fp32" else None
+    traffic = stored_traffic(launch_key) if args.scales == "fp32" and fused else None
+    kname = "gate/up GEMM + activation (fused)" if fused else "grouped_gemm_fp8 (gate/up)"
     pct = lambda q: round(float(np.percentile(step_ms, q)), 4)
     result = {
         "metric": METRIC,
@@ -346,7 +353,8 @@ def main():
                                f"{'masked' if cfg.layout else 'contiguous'} layout",
                    "experts": E, "hidden": H, "intermediate": I, "tokens": T,
                    "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total,
-                   "experts_with_rows": live, "block_scales": args.scales},
+                   "experts_with_rows": live, "block_scales": args.scales,
+                   "gate_up_activation": "fused" if fused else "separate calls"},
         "timing": {"mode": "hipgraph replay" if graph is not None else "eager launches",
                    "cache_flush_mib": args.flush_mib,
                    "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90)},
@@ -354,8 +362,9 @@ def main():
         "token_rows_per_s": round(R / (ms * 1e-3), 1),
     }
     if per is not None:
-        g1 = flops1 / (per["gemm1_gate_up"] * 1e-3) / 1e12
-        g1_gbs = bytes_g1 / (per["gemm1_gate_up"] * 1e-3) / 1e9
+        t1 = per[names[1]]
+        g1 = flops1 / (t1 * 1e-3) / 1e12
+        g1_gbs = bytes_g1 / (t1 * 1e-3) / 1e9
         result["per_kernel_ms"] = {k: round(v, 4) for k, v in per.items()}
         result["per_kernel_rate"] = {
             "gemm1_tflops": round(g1, 1),
@@ -363,19 +372,21 @@ def main():
             "gemm2_tflops": round(flops2 / (per["gemm2_down"] * 1e-3) / 1e12, 1),
             "gemm2_gbs": round(bytes_g2 / (per["gemm2_down"] * 1e-3) / 1e9, 1),
             "dispatch_gbs": round(bytes_perm / (per["dispatch_layout"] * 1e-3) / 1e9, 1),
-            "act_gbs": round(bytes_act / (per["act_requant"] * 1e-3) / 1e9, 1),
             "combine_gbs": round(bytes_comb / (per["combine"] * 1e-3) / 1e9, 1),
         }
+        if not fused:
+            result["per_kernel_rate"]["act_gbs"] = round(
+                bytes_act / (per["act_requant"] * 1e-3) / 1e9, 1)
         # GEMM1 dominates every workload; below the ridge point (peak flop/s over
         # peak bytes/s) its bound is weight streaming from HBM
         ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         if flops1 / bytes_g1 >= ridge:
-            result["roofline"] = {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "mfma",
+            result["roofline"] = {"kernel": kname, "bound": "mfma",
                                   "achieved": round(g1, 2), "peak": FP8_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(g1 / FP8_PEAK_TFLOPS, 4),
                                   "traffic": traffic}
         else:
-            result["roofline"] = {"kernel": "grouped_gemm_fp8 (gate/up)", "bound": "hbm",
+            result["roofline"] = {"kernel": kname, "bound": "hbm",
                                   "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic}

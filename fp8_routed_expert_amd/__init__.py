@@ -6,6 +6,7 @@ from .ops import (moe_layout_workspace_bytes, moe_dispatch_layout,  # noqa: F401
                   moe_grouped_gemm_fp8, moe_gemm_fp8, moe_act_requant, moe_combine,
                   moe_quantize_fp8, moe_quantize_fp8_e8m0, moe_dispatch_layout_e8m0,
                   moe_grouped_gemm_fp8_e8m0, moe_act_requant_e8m0,
+                  moe_gate_up_act_fp8, moe_gate_up_act_fp8_e8m0,
                   LAYOUT_CONTIGUOUS, LAYOUT_MASKED,
                   ERR_BAD_EXPERT, ERR_OVERFLOW, ERR_BAD_INDEX)
 from .layer import MoELayer, contiguous_rows  # noqa: F401

@@ -39,6 +39,10 @@ SIGNATURES = {
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "moe_gemm_fp8": (ctypes.c_int32, [
         _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_gate_up_act_fp8": (ctypes.c_int32, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "moe_gate_up_act_fp8_e8m0": (ctypes.c_int32, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "moe_act_requant": (ctypes.c_int32, [
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "moe_combine": (ctypes.c_int32, [
@@ -47,7 +51,7 @@ SIGNATURES = {
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 

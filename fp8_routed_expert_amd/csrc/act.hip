@@ -18,25 +18,6 @@ namespace moe {
 constexpr int kActThreads = 256;
 constexpr int kActCols = kActThreads * 8;   // columns per workgroup
 
-// silu(g) * u in fp32: exp(-g) as the hardware base-2 exponential of
-// -g log2(e), and the hardware reciprocal (each good to about 1 ulp).
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
-// v / s correctly rounded, from y = RN(1/s): q0 = RN(v y) is within an ulp,
-// the residual v - s q0 is then exact in one fma, and q0 + residual * y
-// rounds to the correctly rounded quotient (Markstein's division theorem).
-// Exactness of the residual needs its bits above the fp32 underflow range;
-// for s >= 2^-90 that holds whenever |v / s| >= 2^-11, and smaller quotients
-// encode to zero in E4M3 either way.  Smaller scales take a real division.
-__device__ __forceinline__ float div_scale(float v, float s, float y) {
-  const float q0 = v * y;
-  const float r = fmaf(-s, q0, v);
-  return fmaf(r, y, q0);
-}
-
 // Is permuted row m inside an expert segment?  Binary search for the last
 // segment start <= m, then check that segment's valid range.
 __device__ __forceinline__ bool row_valid(const int32_t* offsets, const int32_t* counts,
@@ -80,39 +61,19 @@ __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
   }
   amax = group16_max(amax);   // all 16 lanes of a block share in_row
   if (!in_row) return;
-  if (kPow2) {
-    const int e = e8m0_exponent(amax);
-    const float inv = e8m0_inverse(e);
-    uint2 out;
-    out.x = pack2_e4m3(v[0] * inv, v[1] * inv) | (pack2_e4m3(v[2] * inv, v[3] * inv) << 16);
-    out.y = pack2_e4m3(v[4] * inv, v[5] * inv) | (pack2_e4m3(v[6] * inv, v[7] * inv) << 16);
-    *reinterpret_cast<uint2*>(q + (size_t)m * I + j0) = out;
-    if ((threadIdx.x & 15) == 0) {
-      const int jb = j0 / kBlock, ib = I / kBlock;
-      uint8_t* w = reinterpret_cast<uint8_t*>(q_scale) +
-                   ((size_t)(jb >> 2) * rows_total + m) * 4;
-      w[jb & 3] = (uint8_t)(e + 127);
-      if (jb == ib - 1)
-        for (int p = (jb & 3) + 1; p < 4; ++p) w[p] = 127;   // past the last block
-    }
-    return;
-  }
-  const float sc = block_scale(amax);
-  float qv[8];
-  if (sc >= 0x1p-90f) {
-    const float y = 1.0f / sc;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = div_scale(v[i], sc, y);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = v[i] / sc;
-  }
   uint2 out;
-  out.x = pack2_e4m3(qv[0], qv[1]) | (pack2_e4m3(qv[2], qv[3]) << 16);
-  out.y = pack2_e4m3(qv[4], qv[5]) | (pack2_e4m3(qv[6], qv[7]) << 16);
+  const uint32_t sc = requant8<kPow2>(v, amax, out);
   *reinterpret_cast<uint2*>(q + (size_t)m * I + j0) = out;
-  if ((threadIdx.x & 15) == 0)
-    reinterpret_cast<float*>(q_scale)[(size_t)(j0 / kBlock) * rows_total + m] = sc;
+  if ((threadIdx.x & 15) != 0) return;
+  if (kPow2) {
+    const int jb = j0 / kBlock, ib = I / kBlock;
+    uint8_t* w = reinterpret_cast<uint8_t*>(q_scale) + ((size_t)(jb >> 2) * rows_total + m) * 4;
+    w[jb & 3] = (uint8_t)sc;
+    if (jb == ib - 1)
+      for (int p = (jb & 3) + 1; p < 4; ++p) w[p] = 127;   // past the last block
+  } else {
+    reinterpret_cast<uint32_t*>(q_scale)[(size_t)(j0 / kBlock) * rows_total + m] = sc;
+  }
 }
 
 }  // namespace moe

@@ -84,6 +84,54 @@ __device__ __forceinline__ float block_scale(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;
 }
 
+// silu(g) * u in fp32: exp(-g) as the hardware base-2 exponential of
+// -g log2(e), and the hardware reciprocal (each good to about 1 ulp).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// v / s correctly rounded, from y = RN(1/s): q0 = RN(v y) is within an ulp,
+// the residual v - s q0 is then exact in one fma, and q0 + residual * y
+// rounds to the correctly rounded quotient (Markstein's division theorem).
+// Exactness of the residual needs its bits above the fp32 underflow range;
+// for s >= 2^-90 that holds whenever |v / s| >= 2^-11, and smaller quotients
+// encode to zero in E4M3 either way.  Smaller scales take a real division.
+__device__ __forceinline__ float div_scale(float v, float s, float y) {
+  const float q0 = v * y;
+  const float r = fmaf(-s, q0, v);
+  return fmaf(r, y, q0);
+}
+
+// Eight values of one 1x128 block, whose |max| over the whole block is
+// amax, to E4M3 codes (little-endian in out).  Returns the block's scale:
+// fp32 s = amax / 448 (bits), or with kPow2 the biased E8M0 exponent byte.
+// Shared by the stand-alone activation kernel and the fused gate/up
+// epilogue, so both produce the same codes.
+template <bool kPow2>
+__device__ __forceinline__ uint32_t requant8(const float v[8], float amax, uint2& out) {
+  if (kPow2) {
+    const int e = e8m0_exponent(amax);
+    const float inv = e8m0_inverse(e);
+    out.x = pack2_e4m3(v[0] * inv, v[1] * inv) | (pack2_e4m3(v[2] * inv, v[3] * inv) << 16);
+    out.y = pack2_e4m3(v[4] * inv, v[5] * inv) | (pack2_e4m3(v[6] * inv, v[7] * inv) << 16);
+    return (uint32_t)(e + 127);
+  }
+  const float sc = block_scale(amax);
+  float qv[8];
+  if (sc >= 0x1p-90f) {
+    const float y = 1.0f / sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = div_scale(v[i], sc, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = v[i] / sc;
+  }
+  out.x = pack2_e4m3(qv[0], qv[1]) | (pack2_e4m3(qv[2], qv[3]) << 16);
+  out.y = pack2_e4m3(qv[4], qv[5]) | (pack2_e4m3(qv[6], qv[7]) << 16);
+  return __float_as_uint(sc);
+}
+
 // Valid row range of expert e: [start, end) inside the segment and buffer.
 // Returns false (and flags) when the segment description is outside the
 // buffer; the range is then clipped so callers never index out of bounds.

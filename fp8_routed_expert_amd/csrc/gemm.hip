@@ -192,7 +192,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
-    int E, int rows_total, int N, int K, uint16_t* __restrict__ C) {
+    int E, int rows_total, int N, int K, uint16_t* __restrict__ C,
+    uint8_t* __restrict__ Q, void* __restrict__ QS) {
   constexpr int NWM = BM / WM;
   constexpr int NWN = BN / WN;
   constexpr int NW = NWM * NWN;
@@ -207,7 +208,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
   static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
   static_assert(CA < 64, "vmcnt range");
-  (void)kTag;
+  // kTag 4: gate/up projection with the activation and its re-quantisation
+  // fused into the epilogue (W13 rows [0, N/2) gate, [N/2, N) up).  Tile
+  // column block wn holds 32 gate columns followed by the 32 up columns of
+  // the same intermediate columns, so one lane holds both operands of every
+  // silu(gate) * up it produces; a tile covers BN / 2 = 128 intermediate
+  // columns, exactly one 1x128 scale block per row.
+  constexpr bool kFused = kTag == 4;
+  static_assert(!kFused || (WN == 64 && NJ == 4 && BN / 2 == kBlock), "fused tile shape");
 
   // A rows: three stages (k-blocks kb, kb + 1 landed or landing, kb + 2
   // in flight); B rows: two stages.  Each stage is its own LDS object.
@@ -253,7 +261,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int wn = wave - wm * NWN;
   const int Kb = K / kBK;
   const int nb_w = N / kBlock;
-  const int n0 = tile_n * BN;
+  const int n0 = tile_n * BN;                 // first output column (unfused)
+  const int Ih = N / 2;                        // fused: intermediate size
+  const int ni0 = tile_n * (BN / 2);           // fused: first intermediate column
 
   const uint32_t lane_row = (uint32_t)(lane >> 3) * (uint32_t)K;
   const uint32_t lane_off0 = lane_row + (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4);
@@ -261,7 +271,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const long long a_bytes = (long long)(rows_total - row0) * K;
   const v4i rsrc_a = make_rsrc(A + (size_t)row0 * K,
                                (uint32_t)(a_bytes > 0x7ffff000LL ? 0x7ffff000LL : a_bytes));
-  const v4i rsrc_b = make_rsrc(W + ((size_t)e_sel * N + n0) * K, (uint32_t)(BN * K));
+  // fused: the descriptor spans the expert's whole W13 (the host checks
+  // N * K < 2^31); the gate and up rows of a tile are two separate runs
+  const v4i rsrc_b = kFused ? make_rsrc(W + (size_t)e_sel * N * K, (uint32_t)(N * K))
+                            : make_rsrc(W + ((size_t)e_sel * N + n0) * K, (uint32_t)(BN * K));
 
   // Row scales go straight to registers: lane (g, r) needs the scale of row
   // wm*WM + i*16 + r for each subtile row i, loaded one step ahead into
@@ -272,6 +285,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // MFMA applies them itself.
   const int Kw = (Kb + 3) / 4;
   const float* SWw = SW + ((size_t)e_sel * nb_w + (n0 + wn * WN) / kBlock) * (kPow2 ? Kw : Kb);
+  // fused: gate (SWw) and up (SWu) weight blocks of this wave's columns
+  const float* SWg = SW + ((size_t)e_sel * nb_w + (ni0 + wn * (WN / 2)) / kBlock) * (kPow2 ? Kw : Kb);
+  const float* SWu =
+      SW + ((size_t)e_sel * nb_w + (Ih + ni0 + wn * (WN / 2)) / kBlock) * (kPow2 ? Kw : Kb);
   const long long sa_bytes = (long long)(kPow2 ? Kw : Kb) * rows_total * 4;
   const v4i rsrc_s = make_rsrc(SA, (uint32_t)(sa_bytes > 0x7ffff000LL ? 0x7ffff000LL : sa_bytes));
   const int g = lane >> 4;
@@ -306,8 +323,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int c = wave * CB + u;
+      int row = c * 8;   // B row of the tile's first LDS row in this chunk
+      if (kFused) {      // tile column b -> W13 row (gate or up)
+        const int wv = row / WN, k = row - wv * WN;
+        row = (k < WN / 2 ? 0 : Ih - WN / 2) + ni0 + wv * (WN / 2) + k;
+      }
       dma16(rsrc_b, tB + c * 1024,
-            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K + kofs);
+            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)row * (uint32_t)K + kofs);
     }
   };
 
@@ -316,7 +338,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float sw_cur = 0.f;   // weight-block scale of the current step
+  float sw_cur = 0.f;   // weight-block scale of the current step (fused: gate)
+  float swu_cur = 0.f;  // fused: up weight-block scale
 
   // One K step: A k-block kb in A stage SAi = kb % 3, B in B stage
   // SBi = kb % 2.  At its start the B rows and row scales of k-block kb + 1
@@ -342,10 +365,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
     const float sw = sw_cur;
-    sw_cur = rb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+    const float swu = swu_cur;
+    if (kFused) {
+      sw_cur = rb ? SWg[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+      swu_cur = rb ? SWu[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+    } else {
+      sw_cur = rb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+    }
     if constexpr (kPow2) {
       const int sh = 8 * (kb & 3);
       const int sw_e = (int)((__float_as_uint(sw) >> sh) & 0xffu);
+      const int swu_e = kFused ? (int)((__float_as_uint(swu) >> sh) & 0xffu) : sw_e;
       int sa_e[MI];
 #pragma unroll
       for (int i = 0; i < MI; ++i) sa_e[i] = (int)((__float_as_uint(fs[i]) >> sh) & 0xffu);
@@ -357,36 +387,40 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[j], af, acc[i][j], 0, 0, 0, sw_e, 0, sa_e[i]);
+              bf[j], af, acc[i][j], 0, 0, 0, (kFused && j >= NJ / 2) ? swu_e : sw_e, 0,
+              sa_e[i]);
       }
     } else {
     v4f tprev[NJ];
-    float fprev = 0.f;
+    float fprev = 0.f, fprevu = 0.f;
     v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
     for (int i = 0; i <= MI; ++i) {
       v4f tcur[NJ];
-      float fcur = 0.f;
+      float fcur = 0.f, fcuru = 0.f;
       if (i < MI) {
         const v8i af = af_next;
         if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
         fcur = fs[i] * sw;
+        if (kFused) fcuru = fs[i] * swu;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(bf[j], af);
       }
       if (i > 0) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          acc[i - 1][j][0] = fmaf(tprev[j][0], fprev, acc[i - 1][j][0]);
-          acc[i - 1][j][1] = fmaf(tprev[j][1], fprev, acc[i - 1][j][1]);
-          acc[i - 1][j][2] = fmaf(tprev[j][2], fprev, acc[i - 1][j][2]);
-          acc[i - 1][j][3] = fmaf(tprev[j][3], fprev, acc[i - 1][j][3]);
+          const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
+          acc[i - 1][j][0] = fmaf(tprev[j][0], f, acc[i - 1][j][0]);
+          acc[i - 1][j][1] = fmaf(tprev[j][1], f, acc[i - 1][j][1]);
+          acc[i - 1][j][2] = fmaf(tprev[j][2], f, acc[i - 1][j][2]);
+          acc[i - 1][j][3] = fmaf(tprev[j][3], f, acc[i - 1][j][3]);
         }
       }
       if (i < MI) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
         fprev = fcur;
+        fprevu = fcuru;
       }
       if (i > 0 && i < MI) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -410,7 +444,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     lds_barrier();
   };
 
-  sw_cur = SWw[0];
+  if (kFused) {
+    sw_cur = SWg[0];
+    swu_cur = SWu[0];
+  } else {
+    sw_cur = SWw[0];
+  }
   issue_b(0, sB0);
   load_scales(0);
   issue_a(0, sA0);
@@ -433,62 +472,138 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     if (kb + 5 < Kb) step(kb + 5, I2(), I1());
   }
 
-  // ---- epilogue.  In subtile (i, j) a lane holds row r16 and columns
-  // 4g .. 4g+3.  Stored directly, every store instruction would write 16
-  // scattered 32-byte pieces; instead each wave stages its WM x WN bf16
-  // sub-tile (rows of WN * 2 = 128 bytes) in a region of its own in the
-  // stage memory -- free now: the last step waited for every load and ended
-  // with a barrier -- and stores it back as 16-byte pieces, eight lanes per
-  // contiguous 128-byte row.  Only the wave's own LDS accesses are ordered,
-  // so no workgroup barrier is needed.  The 8-byte chunks of staged row r
-  // are XOR-permuted by 2 * ((r >> 1) & 7), which keeps the chunk pairs of
-  // a 16-byte read together.  The output is written with non-temporal
-  // stores.  Measured at the prefill shape: GEMM2 -5%, GEMM1 -4% against
-  // direct 8-byte stores; the packed hardware conversion to bf16 took
-  // another 6% (GEMM2) and 3% (GEMM1) off against a bit-level rounding
-  // sequence.
-  constexpr int kRegion = WM * WN * 2;
-  constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
-  static_assert(WN * 2 == 128, "staged rows are 128 bytes");
-  static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 3 * kPerA + 2 * kPerB, "staging space");
-  uint8_t* region;
-  {
-    int w = wave;
-    if (w < kPerA) {
-      region = sA0 + w * kRegion;
-    } else if ((w -= kPerA) < kPerA) {
-      region = sA1 + w * kRegion;
-    } else if ((w -= kPerA) < kPerA) {
-      region = sA2 + w * kRegion;
-    } else if ((w -= kPerA) < kPerB) {
-      region = sB0 + w * kRegion;
-    } else {
-      region = sB1 + (w - kPerB) * kRegion;
+  if constexpr (kFused) {
+    // ---- fused epilogue.  h = bf16(acc) -- the values the unfused path
+    // stores -- then v = silu(gate) * up in fp32 exactly as the stand-alone
+    // activation kernel computes it, the row's 1x128 amax over the NWN waves
+    // through LDS, E4M3 codes staged in LDS (16-byte chunks XOR-permuted by
+    // row & 7) and stored as 128-byte row pieces, one scale per row.  The
+    // stage memory is free: the last step waited for every load and ended
+    // with a barrier.
+    (void)C;
+    constexpr int NT = 64 * NW;
+    static_assert(BM * NWN * 4 <= SA_B && BM * kBlock <= SA_B, "fused staging space");
+    float* red = reinterpret_cast<float*>(sA1);   // [BM][NWN] partial amax
+    uint8_t* qst = sA0;                            // [BM][128] codes
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      float amax = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < NJ / 2; ++jj) {
+        const uint32_t g01 = pack2_bf16(acc[i][jj][0], acc[i][jj][1]);
+        const uint32_t g23 = pack2_bf16(acc[i][jj][2], acc[i][jj][3]);
+        const uint32_t u01 = pack2_bf16(acc[i][jj + NJ / 2][0], acc[i][jj + NJ / 2][1]);
+        const uint32_t u23 = pack2_bf16(acc[i][jj + NJ / 2][2], acc[i][jj + NJ / 2][3]);
+        acc[i][jj][0] = silu_mul(bf16_to_f32(g01 & 0xffffu), bf16_to_f32(u01 & 0xffffu));
+        acc[i][jj][1] = silu_mul(bf16_to_f32(g01 >> 16), bf16_to_f32(u01 >> 16));
+        acc[i][jj][2] = silu_mul(bf16_to_f32(g23 & 0xffffu), bf16_to_f32(u23 & 0xffffu));
+        acc[i][jj][3] = silu_mul(bf16_to_f32(g23 >> 16), bf16_to_f32(u23 >> 16));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(acc[i][jj][0]), fabsf(acc[i][jj][1])),
+                                 fmaxf(fabsf(acc[i][jj][2]), fabsf(acc[i][jj][3]))));
+      }
+      // the four lanes (g = 0..3) of row r16 hold this wave's 32 columns
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if (g == 0) red[(wm * WM + i * 16 + r16) * NWN + wn] = amax;
     }
-  }
+    lds_barrier();
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int r = i * 16 + r16;
-    const int f = ((r >> 1) & 7) << 1;
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * WM + i * 16 + r16;   // tile row
+      float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      uint2 o;
-      o.x = pack2_bf16(acc[i][j][0], acc[i][j][1]);
-      o.y = pack2_bf16(acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(region + r * 128 + (((j * 4 + g) ^ f) << 3)) = o;
+      for (int w = 0; w < NWN; ++w) amax = fmaxf(amax, red[r * NWN + w]);
+      const float v[8] = {acc[i][0][0], acc[i][0][1], acc[i][0][2], acc[i][0][3],
+                          acc[i][1][0], acc[i][1][1], acc[i][1][2], acc[i][1][3]};
+      uint2 out;
+      const uint32_t sc = requant8<kPow2>(v, amax, out);
+      // out.x: columns wn*32 + 4g .. +3, out.y: wn*32 + 16 + 4g .. +3
+      *reinterpret_cast<uint32_t*>(qst + r * kBlock + (((2 * wn) ^ (r & 7)) << 4) + 4 * g) = out.x;
+      *reinterpret_cast<uint32_t*>(qst + r * kBlock + (((2 * wn + 1) ^ (r & 7)) << 4) + 4 * g) =
+          out.y;
+      const int row = row0 + r;
+      if (wn == 0 && g == 0 && row < row_end) {
+        if (kPow2) {
+          const int jb = ni0 / kBlock, ib = Ih / kBlock;
+          uint8_t* wp = reinterpret_cast<uint8_t*>(QS) + ((size_t)(jb >> 2) * rows_total + row) * 4;
+          wp[jb & 3] = (uint8_t)sc;
+          if (jb == ib - 1)
+            for (int q = (jb & 3) + 1; q < 4; ++q) wp[q] = 127;   // past the last block
+        } else {
+          reinterpret_cast<uint32_t*>(QS)[(size_t)(ni0 / kBlock) * rows_total + row] = sc;
+        }
+      }
     }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  const int c16 = lane & 7;
+    lds_barrier();
 #pragma unroll
-  for (int rr = 0; rr < WM; rr += 8) {
-    const int r = rr + (lane >> 3);
-    const uint4 v =
-        *reinterpret_cast<const uint4*>(region + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
-    const int row = row0 + wm * WM + r;
-    if (row < row_end)   // streamed out: not kept in the caches the tiles share
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
-                                  reinterpret_cast<u32x4*>(C + (size_t)row * N + n0 + wcol + c16 * 8));
+    for (int p = tid; p < BM * 8; p += NT) {
+      const int r = p >> 3, c = p & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(qst + r * kBlock + ((c ^ (r & 7)) << 4));
+      const int row = row0 + r;
+      if (row < row_end)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                    reinterpret_cast<u32x4*>(Q + (size_t)row * Ih + ni0 + c * 16));
+    }
+  } else {
+    (void)Q;
+    (void)QS;
+    // ---- epilogue.  In subtile (i, j) a lane holds row r16 and columns
+    // 4g .. 4g+3.  Stored directly, every store instruction would write 16
+    // scattered 32-byte pieces; instead each wave stages its WM x WN bf16
+    // sub-tile (rows of WN * 2 = 128 bytes) in a region of its own in the
+    // stage memory -- free now: the last step waited for every load and ended
+    // with a barrier -- and stores it back as 16-byte pieces, eight lanes per
+    // contiguous 128-byte row.  Only the wave's own LDS accesses are ordered,
+    // so no workgroup barrier is needed.  The 8-byte chunks of staged row r
+    // are XOR-permuted by 2 * ((r >> 1) & 7), which keeps the chunk pairs of
+    // a 16-byte read together.  The output is written with non-temporal
+    // stores.  Measured at the prefill shape: GEMM2 -5%, GEMM1 -4% against
+    // direct 8-byte stores; the packed hardware conversion to bf16 took
+    // another 6% (GEMM2) and 3% (GEMM1) off against a bit-level rounding
+    // sequence.
+    constexpr int kRegion = WM * WN * 2;
+    constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
+    static_assert(WN * 2 == 128, "staged rows are 128 bytes");
+    static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 3 * kPerA + 2 * kPerB, "staging space");
+    uint8_t* region;
+    {
+      int w = wave;
+      if (w < kPerA) {
+        region = sA0 + w * kRegion;
+      } else if ((w -= kPerA) < kPerA) {
+        region = sA1 + w * kRegion;
+      } else if ((w -= kPerA) < kPerA) {
+        region = sA2 + w * kRegion;
+      } else if ((w -= kPerA) < kPerB) {
+        region = sB0 + w * kRegion;
+      } else {
+        region = sB1 + (w - kPerB) * kRegion;
+      }
+    }
+  #pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = i * 16 + r16;
+      const int f = ((r >> 1) & 7) << 1;
+  #pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        uint2 o;
+        o.x = pack2_bf16(acc[i][j][0], acc[i][j][1]);
+        o.y = pack2_bf16(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<uint2*>(region + r * 128 + (((j * 4 + g) ^ f) << 3)) = o;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c16 = lane & 7;
+  #pragma unroll
+    for (int rr = 0; rr < WM; rr += 8) {
+      const int r = rr + (lane >> 3);
+      const uint4 v =
+          *reinterpret_cast<const uint4*>(region + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
+      const int row = row0 + wm * WM + r;
+      if (row < row_end)   // streamed out: not kept in the caches the tiles share
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                    reinterpret_cast<u32x4*>(C + (size_t)row * N + n0 + wcol + c16 * 8));
+    }
   }
 }
 
@@ -496,7 +611,8 @@ template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2 = false>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
-                           uint16_t* c, hipStream_t st) {
+                           uint16_t* c, hipStream_t st, uint8_t* q = nullptr,
+                           void* q_scale = nullptr) {
   if (N % BN != 0) return MOE_UNSUPPORTED_SHAPE;
   long long m_tiles = kTag == 3 ? ((long long)rows_total + BM - 1) / BM
                                 : (long long)rows_total / BM + E;
@@ -506,7 +622,7 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
   hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag, kPow2>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
-                     offsets, counts, E, rows_total, N, K, c);
+                     offsets, counts, E, rows_total, N, K, c, q, q_scale);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
@@ -521,6 +637,13 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 #endif
 #ifndef MOE_GEMM_SMALL
 #define MOE_GEMM_SMALL 128, 128, 64, 64, 4
+#endif
+// The fused gate/up + activation kernel needs a tile to cover one whole
+// 1x128 block of intermediate columns (BN = 256: 128 gate + 128 up
+// columns): large problems use MOE_GEMM_BIG, small ones 128 x 256 tiles of
+// 8 waves of 64 x 64 (one workgroup per CU).
+#ifndef MOE_GEMM_FUSED_SMALL
+#define MOE_GEMM_FUSED_SMALL 128, 256, 64, 64, 2
 #endif
 
 }  // namespace moe
@@ -572,6 +695,53 @@ extern "C" moe_status_t moe_grouped_gemm_fp8_e8m0(
   return grouped_gemm<true>(a, reinterpret_cast<const float*>(a_scale), w,
                             reinterpret_cast<const float*>(w_scale), offsets, counts, E,
                             rows_total, N, K, c, stream);
+}
+
+template <bool kPow2>
+static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const uint8_t* w13,
+                                const float* w13_scale, const int32_t* offsets,
+                                const int32_t* counts, int E, int rows_total, int I, int H,
+                                uint8_t* q2, void* q2_scale, void* stream) {
+  if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0 || H <= 0)
+    return MOE_INVALID_ARG;
+  if (I % kBlock != 0 || H % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
+  if (2LL * I * H > 0x7ffff000LL) return MOE_UNSUPPORTED_SHAPE;   // one expert's W13 < 2 GB
+  if (!offsets || !counts || !w13 || !w13_scale) return MOE_INVALID_ARG;
+  if (rows_total == 0) return MOE_OK;
+  if (!a || !a_scale || !q2 || !q2_scale) return MOE_INVALID_ARG;
+  if (((uintptr_t)a | (uintptr_t)w13 | (uintptr_t)q2) & 15) return MOE_UNSUPPORTED_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int N = 2 * I;
+  // the same host-side rule as the unfused gate/up GEMM
+  const bool big = (long long)(rows_total / 256) * (N / 256) >= 512;
+  if (big)
+    return launch<MOE_GEMM_BIG, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
+                                          rows_total, N, H, nullptr, st, q2, q2_scale);
+  return launch<MOE_GEMM_FUSED_SMALL, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
+                                                rows_total, N, H, nullptr, st, q2, q2_scale);
+}
+
+extern "C" moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_scale,
+                                            const uint8_t* w13, const float* w13_scale,
+                                            const int32_t* offsets, const int32_t* counts,
+                                            int E, int rows_total, int I, int H, uint8_t* q2,
+                                            float* q2_scale, int32_t* status_dev,
+                                            void* stream) {
+  (void)status_dev;
+  return gate_up_act<false>(a, a_scale, w13, w13_scale, offsets, counts, E, rows_total, I, H,
+                            q2, q2_scale, stream);
+}
+
+extern "C" moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
+                                                 const uint8_t* w13, const uint32_t* w13_scale,
+                                                 const int32_t* offsets, const int32_t* counts,
+                                                 int E, int rows_total, int I, int H,
+                                                 uint8_t* q2, uint32_t* q2_scale,
+                                                 int32_t* status_dev, void* stream) {
+  (void)status_dev;
+  return gate_up_act<true>(a, reinterpret_cast<const float*>(a_scale), w13,
+                           reinterpret_cast<const float*>(w13_scale), offsets, counts, E,
+                           rows_total, I, H, q2, q2_scale, stream);
 }
 
 extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* w,

@@ -1,10 +1,17 @@
 """A routed-expert MoE layer share that owns its device buffers.
 
 MoELayer allocates every intermediate once (torch device memory) and runs
-the five library calls of one layer on a stream:
+the library calls of one layer on a stream:
 
-  moe_dispatch_layout -> moe_grouped_gemm_fp8 (gate/up) -> moe_act_requant
+  moe_dispatch_layout -> moe_gate_up_act_fp8 (gate/up GEMM + activation)
   -> moe_grouped_gemm_fp8 (down) -> moe_combine
+
+With fuse_act=False the gate/up GEMM and the activation run as two calls
+(moe_grouped_gemm_fp8 -> moe_act_requant) through a bf16 buffer h; both
+orders give the same q2 bit for bit.  fuse_act="auto" (the default) fuses
+when the library runs the gate/up GEMM with its large 256 x 256 tiles (the
+same size rule as the library's); at decode sizes the two calls measured
+faster (the fused kernel needs 128 x 256 tiles there, one workgroup per CU).
 
 All arithmetic happens in the HIP library; this class only holds memory.
 The call sequence allocates nothing and reads nothing back, so it can be
@@ -25,17 +32,28 @@ def contiguous_rows(R, E, align_m=128):
     return int(R) + E * (align_m - 1)
 
 
+def big_gate_up_tiles(rows_total, I):
+    """Whether the library runs the gate/up GEMM of this buffer with its
+    256 x 256 tiles: at least 512 full tiles (its host-side rule)."""
+    return (int(rows_total) // 256) * (2 * int(I) // 256) >= 512
+
+
 class MoELayer:
     def __init__(self, E, H, I, T, K, layout, rows, align_m=128, device="cuda",
-                 scale_fmt="fp32"):
+                 scale_fmt="fp32", fuse_act="auto"):
         """rows: M_cap for the contiguous layout, capacity C for masked."""
         if scale_fmt not in ("fp32", "e8m0"):
             raise ValueError(f"scale_fmt {scale_fmt!r}")
+        if fuse_act not in ("auto", True, False):
+            raise ValueError(f"fuse_act {fuse_act!r}")
         self.scale_fmt = scale_fmt
         self.E, self.H, self.I, self.T, self.K = E, H, I, T, K
         self.layout, self.rows, self.align_m = layout, rows, align_m
         self.rows_total = E * rows if layout == ops.LAYOUT_MASKED else rows
         R, d = self.rows_total, device
+        if fuse_act == "auto":
+            fuse_act = big_gate_up_tiles(R, I)
+        self.fuse_act = bool(fuse_act)
         i32 = dict(dtype=torch.int32, device=d)
         self.counts = torch.zeros(E, **i32)
         self.offsets = torch.zeros(E + 1, **i32)
@@ -47,7 +65,9 @@ class MoELayer:
         sdt = torch.int32 if pk else torch.float32
         self.a_scale = torch.zeros((H // 128 + 3) // 4 if pk else H // 128, R, dtype=sdt,
                                    device=d)
-        self.h = torch.zeros(R, 2 * I, dtype=torch.bfloat16, device=d)
+        # h exists only on the unfused path
+        self.h = None if self.fuse_act else torch.zeros(R, 2 * I, dtype=torch.bfloat16,
+                                                        device=d)
         self.q2 = torch.zeros(R, I, dtype=torch.uint8, device=d)
         self.q2_scale = torch.zeros((I // 128 + 3) // 4 if pk else I // 128, R, dtype=sdt,
                                     device=d)
@@ -65,8 +85,18 @@ class MoELayer:
           self.workspace, self.status, stream)
 
     def gemm1(self, w13, s13, stream=None):
+        """Unfused path: h = gate/up GEMM (needs fuse_act=False)."""
+        if self.h is None:
+            raise RuntimeError("gemm1/act are the unfused path: build with fuse_act=False")
         self._gemm(self.a, self.a_scale, w13, s13, self.offsets, self.counts, self.h,
                    self.status, stream)
+
+    def gemm1_act(self, w13, s13, stream=None):
+        """Fused path: q2, q2_scale straight from the gate/up GEMM."""
+        f = (ops.moe_gate_up_act_fp8_e8m0 if self.scale_fmt == "e8m0"
+             else ops.moe_gate_up_act_fp8)
+        f(self.a, self.a_scale, w13, s13, self.offsets, self.counts, self.q2, self.q2_scale,
+          self.status, stream)
 
     def _gemm(self, *args):
         f = (ops.moe_grouped_gemm_fp8_e8m0 if self.scale_fmt == "e8m0"
@@ -74,6 +104,8 @@ class MoELayer:
         f(*args)
 
     def act(self, stream=None):
+        if self.h is None:
+            raise RuntimeError("gemm1/act are the unfused path: build with fuse_act=False")
         f = ops.moe_act_requant_e8m0 if self.scale_fmt == "e8m0" else ops.moe_act_requant
         f(self.h, self.offsets, self.counts, self.q2, self.q2_scale, self.status, stream)
 
@@ -87,8 +119,11 @@ class MoELayer:
     def forward(self, topk_idx, x, x_scale, topk_w, w13, s13, w2, s2, stream=None):
         """One full pass S1-S8; returns self.out (bf16 [T, H])."""
         self.dispatch(topk_idx, x, x_scale, stream)
-        self.gemm1(w13, s13, stream)
-        self.act(stream)
+        if self.fuse_act:
+            self.gemm1_act(w13, s13, stream)
+        else:
+            self.gemm1(w13, s13, stream)
+            self.act(stream)
         self.gemm2(w2, s2, stream)
         self.combine(topk_w, stream)
         return self.out

@@ -104,6 +104,43 @@ def moe_gemm_fp8(a, a_scale, w, w_scale, c, stream=None):
     check(st, "moe_gemm_fp8")
 
 
+def _gate_up_act(name, a, a_scale, w13, w13_scale, offsets, counts, q2, q2_scale, status,
+                 stream, packed):
+    E, I2, H = w13.shape
+    I = I2 // 2
+    rows_total = a.shape[0]
+    sdt = _I32 if packed else _F32
+    hw = _words(H // 128) if packed else H // 128
+    iw = _words(I // 128) if packed else I // 128
+    lib = load()
+    st = getattr(lib, name)(
+        _ptr(a, _U8, "a", (rows_total, H)), _ptr(a_scale, sdt, "a_scale", (hw, rows_total)),
+        _ptr(w13, _U8, "w13", (E, I2, H)), _ptr(w13_scale, sdt, "w13_scale", (E, I2 // 128, hw)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)), _ptr(counts, _I32, "counts", (E,)),
+        E, rows_total, I, H, _ptr(q2, _U8, "q2", (rows_total, I)),
+        _ptr(q2_scale, sdt, "q2_scale", (iw, rows_total)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, name)
+
+
+def moe_gate_up_act_fp8(a, a_scale, w13, w13_scale, offsets, counts, q2, q2_scale, status,
+                        stream=None):
+    """q2, q2_scale = moe_act_requant(moe_grouped_gemm_fp8(a, w13)) in one kernel:
+    w13 [E, 2I, H] e4m3 (gate rows first), w13_scale [E, 2I/128, H/128] f32,
+    q2 [rows_total, I] e4m3, q2_scale [I/128, rows_total] f32."""
+    _gate_up_act("moe_gate_up_act_fp8", a, a_scale, w13, w13_scale, offsets, counts, q2,
+                 q2_scale, status, stream, False)
+
+
+def moe_gate_up_act_fp8_e8m0(a, a_scale, w13, w13_scale, offsets, counts, q2, q2_scale,
+                             status, stream=None):
+    """moe_gate_up_act_fp8 with packed scales (int32 words of four E8M0 bytes):
+    a_scale [ceil(H/512), rows_total], w13_scale [E, 2I/128, ceil(H/512)],
+    q2_scale [ceil(I/512), rows_total]."""
+    _gate_up_act("moe_gate_up_act_fp8_e8m0", a, a_scale, w13, w13_scale, offsets, counts, q2,
+                 q2_scale, status, stream, True)
+
+
 def moe_act_requant(h, offsets, counts, q, q_scale, status, stream=None):
     """q, q_scale = E4M3 1x128 requantisation of silu(h[:, :I]) * h[:, I:]."""
     rows_total, I2 = h.shape

@@ -200,6 +200,34 @@ moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
                              int32_t* status_dev, void* stream);
 
 /*
+ * moe_gate_up_act_fp8 — the gate/up grouped GEMM and moe_act_requant fused
+ * into one kernel (the GEMM of "Deploying DeepSeek with PD Disaggregation
+ * and Large-Scale Expert Parallelism on 96 H100 GPUs", section 大规模专家并行
+ * › DeepGEMM 集成, followed by the activation read above).  For every valid
+ * row m the result is exactly that of
+ *   moe_grouped_gemm_fp8(a, a_scale, w13, w13_scale, ..., N = 2I, K = H, h)
+ *   moe_act_requant(h, ..., I, q2, q2_scale)
+ * -- the same codes and scales bit for bit: each h value is rounded to
+ * bf16 as the GEMM stores it before the activation reads it -- but h is
+ * never written to memory.
+ *
+ *   a        [rows_total, H] e4m3      a_scale [H/128, rows_total] f32
+ *   w13      [E, 2I, H] e4m3 (rows [0, I) gate, [I, 2I) up)
+ *   w13_scale [E, 2I/128, H/128] f32
+ *   q2       [rows_total, I] e4m3      q2_scale [I/128, rows_total] f32
+ * I and H must be multiples of 128 and one expert's W13 (2 I H bytes)
+ * below 2 GB (MOE_UNSUPPORTED_SHAPE otherwise); a, w13 and q2 16-byte
+ * aligned.  Rows outside every expert's valid range are not written.
+ * status_dev is accepted for uniformity and not written.
+ */
+moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_scale,
+                                 const uint8_t* w13, const float* w13_scale,
+                                 const int32_t* offsets, const int32_t* counts,
+                                 int E, int rows_total, int I, int H, uint8_t* q2,
+                                 float* q2_scale, int32_t* status_dev,
+                                 void* stream);
+
+/*
  * moe_combine — un-permute and sum each token's rows weighted by its top-k
  * weights [H100-EP 基于 DeepEP 的专家并行: combine returns expert outputs to
  * their source tokens]:
@@ -256,6 +284,10 @@ moe_status_t moe_quantize_fp8(const void* x, int x_is_f32, int rows, int cols,
  *                             w_scale [E, N/128, ceil(K/512)] words;
  *                             c = bf16_rne(sum_kb 2^(ea + ew) * block product)
  *   moe_act_requant_e8m0      q_scale [ceil(I/512), rows_total] words
+ *   moe_gate_up_act_fp8_e8m0  a_scale, w13_scale as the grouped GEMM's,
+ *                             q2_scale [ceil(I/512), rows_total] words;
+ *                             equal to moe_grouped_gemm_fp8_e8m0 followed by
+ *                             moe_act_requant_e8m0
  * Argument checks, status bits and layouts otherwise as above.
  */
 moe_status_t moe_quantize_fp8_e8m0(const void* x, int x_is_f32, int rows,
@@ -278,6 +310,12 @@ moe_status_t moe_act_requant_e8m0(const uint16_t* h, const int32_t* offsets,
                                   const int32_t* counts, int E, int rows_total,
                                   int I, uint8_t* q, uint32_t* q_scale,
                                   int32_t* status_dev, void* stream);
+moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
+                                      const uint8_t* w13, const uint32_t* w13_scale,
+                                      const int32_t* offsets, const int32_t* counts,
+                                      int E, int rows_total, int I, int H,
+                                      uint8_t* q2, uint32_t* q2_scale,
+                                      int32_t* status_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,17 @@ def test_host_argument_errors_launch_nothing():
     assert lib.moe_gemm_fp8(fake, fake, fake, fake, 0, 128, 128, fake, N) == 0
     # act: I not a multiple of 128
     assert lib.moe_act_requant(fake, fake, fake, 2, 16, 100, fake, fake, fake, N) == 2
+    # fused gate/up + act: I or H not a multiple of 128, one expert's W13 of
+    # 2 GB or more, null offsets, misaligned q2, rows_total = 0 is a no-op
+    for f in (lib.moe_gate_up_act_fp8, lib.moe_gate_up_act_fp8_e8m0):
+        assert f(fake, fake, fake, fake, fake, fake, 2, 256, 100, 256, fake, fake, fake, N) == 2
+        assert f(fake, fake, fake, fake, fake, fake, 2, 256, 128, 200, fake, fake, fake, N) == 2
+        assert f(fake, fake, fake, fake, fake, fake, 2, 256, 65536, 16384, fake, fake, fake,
+                 N) == 2
+        assert f(fake, fake, fake, fake, N, fake, 2, 256, 128, 256, fake, fake, fake, N) == 1
+        assert f(fake, fake, fake, fake, fake, fake, 2, 256, 128, 256, ctypes.c_void_p(4097),
+                 fake, fake, N) == 2
+        assert f(fake, fake, fake, fake, fake, fake, 2, 0, 128, 256, fake, fake, fake, N) == 0
     # combine: K too large / H not a multiple of 128
     assert lib.moe_combine(fake, 16, fake, fake, 4, 65, 128, fake, fake, N) == 1
     assert lib.moe_combine(fake, 16, fake, fake, 4, 8, 100, fake, fake, N) == 2
