@@ -164,27 +164,75 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int g) {
   return r;
 }
 
-// Walk the experts' m-tiles (ceil(valid rows / BM) each).  Returns the total
-// number of m-tiles; fills e_sel / row0 / row_end for m-tile `mt` (e_sel = -1
-// if there is no such tile).
+// The experts' m-tiles: expert e has ceil(valid rows / BM) of them,
+// numbered expert by expert.  Each wave evaluates it on its own, 64 experts
+// per pass with lane l holding expert base + l (one round of vector loads,
+// then shuffles), so a tile is located in about one memory latency rather
+// than a chain of dependent scalar loads per expert.  All results are
+// wave-uniform.
+struct SegLane {
+  int s, en, nt;   // this lane's expert: valid rows [s, en), m-tiles
+};
+
 template <int BM>
-__device__ __forceinline__ int find_mtile(const int32_t* offsets, const int32_t* counts,
-                                          int E, int rows_total, int mt, int& e_sel,
-                                          int& row0, int& row_end) {
-  int acc = 0;
-  e_sel = -1;
-  for (int e = 0; e < E; ++e) {
-    int s, en;
-    expert_rows(offsets, counts, e, rows_total, s, en);
-    const int nt = (en - s + BM - 1) / BM;
-    if (e_sel < 0 && mt < acc + nt) {
-      e_sel = e;
-      row0 = s + (mt - acc) * BM;
-      row_end = en;
-    }
-    acc += nt;
+__device__ __forceinline__ SegLane seg_lane(const int32_t* offsets, const int32_t* counts,
+                                            int E, int rows_total, int e) {
+  SegLane r{0, 0, 0};
+  if (e < E) {
+    expert_rows(offsets, counts, e, rows_total, r.s, r.en);
+    r.nt = (r.en - r.s + BM - 1) / BM;
   }
-  return acc;
+  return r;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d);
+    if (lane >= d) x += t;
+  }
+  return x;
+}
+
+// Total number of m-tiles.
+template <int BM>
+__device__ __forceinline__ int total_mtiles(const int32_t* offsets, const int32_t* counts,
+                                            int E, int rows_total, int lane) {
+  int total = 0;
+  for (int base = 0; base < E; base += 64)
+    total += wave_sum(seg_lane<BM>(offsets, counts, E, rows_total, base + lane).nt);
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// Expert, first row and segment end of m-tile mt (e_sel = -1 if none).
+template <int BM>
+__device__ __forceinline__ void find_mtile(const int32_t* offsets, const int32_t* counts,
+                                           int E, int rows_total, int mt, int lane,
+                                           int& e_sel, int& row0, int& row_end) {
+  e_sel = -1;
+  int before = 0;   // m-tiles of the experts of earlier passes
+  for (int base = 0; base < E; base += 64) {
+    const SegLane g = seg_lane<BM>(offsets, counts, E, rows_total, base + lane);
+    const int incl = before + wave_inclusive_scan(g.nt, lane);
+    // the first lane whose running count passes mt holds the expert (its
+    // count is non-zero: the running count steps there)
+    const uint64_t hit = __ballot(incl > mt);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      e_sel = base + l;
+      row0 = __builtin_amdgcn_readlane(g.s, l) +
+             (mt - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(g.nt, l))) * BM;
+      row_end = __builtin_amdgcn_readlane(g.en, l);
+      return;
+    }
+    before = __builtin_amdgcn_readlane(incl, 63);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2>
@@ -232,9 +280,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   constexpr bool kDense = kTag == 3;
   const int n_tiles = N / BN;
   int e_sel = 0, row0 = 0, row_end = 0;
-  const int total_m =
-      kDense ? (rows_total + BM - 1) / BM
-             : find_mtile<BM>(offsets, counts, E, rows_total, 0x7fffffff, e_sel, row0, row_end);
+  const int lane = threadIdx.x & 63;
+  const int total_m = kDense ? (rows_total + BM - 1) / BM
+                             : total_mtiles<BM>(offsets, counts, E, rows_total, lane);
   const int total = total_m * n_tiles;
   const int logical = blockIdx.x;
   if (logical >= total) return;
@@ -250,12 +298,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     row0 = tile_m * BM;
     row_end = rows_total;
   } else {
-    find_mtile<BM>(offsets, counts, E, rows_total, tile_m, e_sel, row0, row_end);
+    find_mtile<BM>(offsets, counts, E, rows_total, tile_m, lane, e_sel, row0, row_end);
     if (e_sel < 0) return;
   }
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / NWN;
   const int wn = wave - wm * NWN;

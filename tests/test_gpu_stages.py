@@ -263,6 +263,29 @@ def test_gemm_exact_integers_pow2_scales(gpu):
             assert np.array_equal(bf16_decode(got[s:en]), ref), e
 
 
+def test_gemm_exact_many_experts(gpu):
+    """More experts than one wave has lanes (the tile lookup then takes
+    several passes of 64 experts): 150 experts, a third of them empty, the
+    rest with 1..40 rows in unaligned segments; exact small-integer data as
+    above, so every valid row must equal the oracle bit for bit."""
+    g = np.random.default_rng(23)
+    E, N, K = 150, 256, 256
+    counts = g.integers(1, 41, E)
+    counts[g.choice(E, E // 3, replace=False)] = 0
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    rows_total = int(offsets[-1]) + 2
+    a = e4m3_encode(g.integers(-4, 5, (rows_total, K)).astype(np.float64))
+    w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
+    sa = np.ldexp(1.0, g.integers(-2, 3, (rows_total, K // 128))).astype(np.float32)
+    sw = np.ldexp(1.0, g.integers(-2, 3, (E, N // 128, K // 128))).astype(np.float32)
+    got = _run_gemm(a, sa, w, sw, offsets, counts, rows_total)
+    for e in range(E):
+        s, en = offsets[e], offsets[e] + counts[e]
+        if en > s:
+            ref = moe.gemm_rows(a[s:en], sa[s:en], w[e], sw[e])
+            assert np.array_equal(bf16_decode(got[s:en]), ref), e
+
+
 def _sample_rows(L, n_per_expert=6, seed=0):
     g = np.random.default_rng(seed)
     rows = []
