@@ -92,8 +92,10 @@ def cpu_baseline(cfg, idx, w, n_tokens):
     rows = int((idx >= 0).sum()) + E * (cfg.align_m - 1)
     kw = dict(capacity=cfg.capacity) if cfg.layout == moe.LAYOUT_MASKED else \
         dict(align_m=cfg.align_m, rows=rows)
+    stages = {}
     t0 = time.perf_counter()
-    res = moe.layer(x, xs, idx, w, w13, s13, w2, s2, cfg.layout, tokens=toks, **kw)
+    res = moe.layer(x, xs, idx, w, w13, s13, w2, s2, cfg.layout, tokens=toks,
+                    stage_seconds=stages, **kw)
     dt = time.perf_counter() - t0
     n_rows = len(res["slots"])
     flops = 2 * n_rows * (2 * cfg.I) * cfg.H + 2 * n_rows * cfg.H * cfg.I
@@ -103,7 +105,8 @@ def cpu_baseline(cfg, idx, w, n_tokens):
             "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} source tokens ({n_rows} routed rows), seeded; "
                       f"layout over all tokens; fp64 numpy, BLAS threads={threads}",
-            "seconds": round(dt, 3), "rows_per_s": n_rows / dt}
+            "seconds": round(dt, 3), "rows_per_s": n_rows / dt,
+            "stage_seconds": {k: round(v, 3) for k, v in stages.items()}}
 
 
 def bench_dense(args, M, N, K):
@@ -189,8 +192,8 @@ def main():
                          "(reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the expert-parallel layer; "
-              "runs on more than one GPU are not part of this build (use --gpus 1).",
+        print("bench.py measures one GPU's share of the expert-parallel layer and "
+              "runs on a single GPU only (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -361,7 +364,20 @@ def main():
         "mfma_peak_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
         "token_rows_per_s": round(R / (ms * 1e-3), 1),
     }
+    # the step's roofline: each stage at the slower of its two bounds (its
+    # flops at the FP8 MFMA peak, its algorithmic bytes at the HBM peak)
+    work = {"dispatch_layout": (0.0, bytes_perm), names[1]: (flops1, bytes_g1),
+            "gemm2_down": (flops2, bytes_g2), "combine": (0.0, bytes_comb)}
+    if not fused:
+        work["act_requant"] = (0.0, bytes_act)
+    bound_ms = {n: 1e3 * max(f / (FP8_PEAK_TFLOPS * 1e12), b / (HBM_PEAK_GBS * 1e9))
+                for n, (f, b) in work.items()}
+    att = sum(bound_ms.values())
+    result["attainable"] = {"step_ms": round(att, 4), "frac": round(att / ms, 4),
+                            "per_kernel_ms": {n: round(bound_ms[n], 4) for n in names}}
     if per is not None:
+        result["attainable"]["per_kernel_frac"] = {
+            n: round(bound_ms[n] / per[n], 4) for n in names}
         t1 = per[names[1]]
         g1 = flops1 / (t1 * 1e-3) / 1e12
         g1_gbs = bytes_g1 / (t1 * 1e-3) / 1e9

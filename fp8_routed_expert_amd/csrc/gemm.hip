@@ -129,6 +129,23 @@ __device__ __forceinline__ void wait_loads(float (&r)[M]) {
   for (int i = 0; i < M; ++i) asm volatile("" : "+v"(r[i]));
 }
 
+// Lane l holds the value of row l of a 64-row block; out[k] receives, in
+// every lane, the value of row 16k + (lane mod 16) -- row group k
+// broadcast to the four groups.  Swapping the upper 32 lanes of one copy
+// with the lower 32 of another gives groups (0 1 0 1) and (2 3 2 3);
+// swapping odd with even groups of each with itself then gives each group
+// in all four positions.
+__device__ __forceinline__ void row_scales(float r, float* out) {
+  const uint32_t v = __float_as_uint(r);
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+  out[0] = __uint_as_float(lo[0]);
+  out[1] = __uint_as_float(lo[1]);
+  out[2] = __uint_as_float(hi[0]);
+  out[3] = __uint_as_float(hi[1]);
+}
+
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   // format 0 = E4M3 for both operands; zero scale operands select the plain
@@ -323,10 +340,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const v4i rsrc_b = kFused ? make_rsrc(W + (size_t)e_sel * N * K, (uint32_t)(N * K))
                             : make_rsrc(W + ((size_t)e_sel * N + n0) * K, (uint32_t)(BN * K));
 
-  // Row scales go straight to registers: lane (g, r) needs the scale of row
-  // wm*WM + i*16 + r for each subtile row i, loaded one step ahead into
-  // fs_next.  Rows past the buffer read another k-block's scales or zero and
-  // only feed rows that are never stored.  kPow2: scales are E8M0 bytes
+  // Row scales go straight to registers, one step ahead: lane l loads the
+  // scales of rows wm*WM + 64c + l (MI / 4 loads, into fs_raw), and the
+  // scale of row wm*WM + i*16 + r that lane (g, r) needs for subtile row i
+  // is then broadcast from lane 16 (i mod 4) + r of load i / 4 by lane swaps
+  // (row_scales).  Rows past the buffer read another k-block's scales or
+  // zero and only feed rows that are never stored.  kPow2: scales are E8M0 bytes
   // packed four k-blocks per 32-bit word (row scales [ceil(Kb/4),
   // rows_total] words, weight scales [E, N/128, ceil(Kb/4)] words); the
   // MFMA applies them itself.
@@ -341,20 +360,22 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int wcol = wn * WN;
-  const uint32_t srow = (uint32_t)(row0 + wm * WM + r16);
-  float fs_next[MI];
+  static_assert(MI % 4 == 0, "row scales are loaded 64 rows at a time");
+  constexpr int NR = MI / 4;
+  const uint32_t srow = (uint32_t)(row0 + wm * WM + lane);
+  float fs_raw[NR];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) fs_next[i] = 0.f;
+  for (int c = 0; c < NR; ++c) fs_raw[c] = 0.f;
   // The loads are inline assembly, like the tile loads: a register is
   // filled when its load completes, not when the instruction issues, so
-  // fs_next is read only after the wait_loads() that covers these loads,
+  // fs_raw is read only after the wait_loads() that covers these loads,
   // which is also where the compiler sees the values being written.
   auto load_scales = [&](int kb) {
     const uint32_t base = ((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total + srow) * 4u;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int c = 0; c < NR; ++c)
       asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3"
-                   : "=v"(fs_next[i]) : "v"(base), "s"(rsrc_s), "n"(i * 64) : "memory");
+                   : "=v"(fs_raw[c]) : "v"(base), "s"(rsrc_s), "n"(c * 256) : "memory");
   };
   auto issue_a = [&](int kb, uint8_t* tA) {
     const uint32_t kofs = (uint32_t)kb * kBK;
@@ -400,7 +421,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     const uint8_t* tB = stB[SBi];
     float fs[MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fs[i] = fs_next[i];
+    for (int c = 0; c < NR; ++c) row_scales(fs_raw[c], fs + 4 * c);
     const bool rb = kb + 1 < Kb;
     const bool ra = kb + 2 < Kb;
     if (rb) {
@@ -485,9 +506,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
       for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
     if (ra)
-      wait_loads<CA>(fs_next);
+      wait_loads<CA>(fs_raw);
     else
-      wait_loads<0>(fs_next);
+      wait_loads<0>(fs_raw);
     lds_barrier();
   };
 
@@ -502,9 +523,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   issue_a(0, sA0);
   if (Kb > 1) {
     issue_a(1, sA1);
-    wait_loads<CA>(fs_next);
+    wait_loads<CA>(fs_raw);
   } else {
-    wait_loads<0>(fs_next);
+    wait_loads<0>(fs_raw);
   }
   lds_barrier();
   using I0 = std::integral_constant<int, 0>;

@@ -41,6 +41,8 @@ All floating point is float64.  Scales are kept in their natural layout
 (activation scales [rows, H/128], weight scales [E, N/128, K/128]).
 """
 
+import time
+
 import numpy as np
 
 from .codec import e4m3_decode, e4m3_encode, bf16_round, E4M3_MAX
@@ -252,7 +254,8 @@ def combine_rows(y_of_slot, slot_of, topk_w, tokens):
 # chained layer (optionally on a subset of source tokens)
 # --------------------------------------------------------------------------
 def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
-          align_m=BLOCK, rows=None, capacity=None, tokens=None, requant=None):
+          align_m=BLOCK, rows=None, capacity=None, tokens=None, requant=None,
+          stage_seconds=None):
     """Run S1-S8 on the CPU.
 
     x [T, H] E4M3 codes, x_scale [T, H/128]; w13 [E, 2I, H], s13
@@ -265,12 +268,23 @@ def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
     those rows `h` [n, 2I], `q2` [n, I], `q2_scale` [n, I/128], `y` [n, H]
     (float64 bf16 values / uint8 codes), plus `tokens` and `out`
     [len(tokens), H].  `requant` replaces S6's quantiser (default
-    act_requant); it maps h to (codes, fp32 block scales).
+    act_requant); it maps h to (codes, fp32 block scales).  `stage_seconds`,
+    if a dict, receives the wall time of each stage (timing only: it changes
+    nothing that is computed).
     """
     requant = act_requant if requant is None else requant
+    clock = {"t": time.perf_counter()}
+
+    def lap(name):
+        now = time.perf_counter()
+        if stage_seconds is not None:
+            stage_seconds[name] = stage_seconds.get(name, 0.0) + now - clock["t"]
+        clock["t"] = now
+
     E = w13.shape[0]
     T = x.shape[0]
     L = dispatch_layout(topk_idx, E, layout, align_m, rows, capacity)
+    lap("S1-S4 layout")
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     so = L["slot_of"][tokens]
     slots = np.unique(so[so >= 0])
@@ -286,14 +300,19 @@ def layer(x, x_scale, topk_idx, topk_w, w13, s13, w2, s2, layout,
         sel = np.nonzero(ex == e)[0]
         if len(sel) == 0:
             continue
+        lap("other")
         xa, xs = x[src[sel]], x_scale[src[sel]]
         h[sel] = gemm_rows(xa, xs, w13[e], s13[e])
+        lap("S5 gate/up GEMM")
         q, qs = requant(h[sel])
         q2[sel], q2s[sel] = q, qs
+        lap("S6 activation")
         y[sel] = gemm_rows(q, qs, w2[e], s2[e])
+        lap("S7 down GEMM")
     pos = {int(s): i for i, s in enumerate(slots)}
     y_of_slot = {s: y[i] for s, i in pos.items()}
     out = combine_rows(y_of_slot, L["slot_of"], topk_w, tokens)
+    lap("S8 combine")
     if out.shape[1] == 0:
         out = np.zeros((len(tokens), H))
     return dict(layout=L, slots=slots, h=h, q2=q2, q2_scale=q2s, y=y,
