@@ -75,6 +75,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
+#ifndef MOE_GEMM_CARRY
+#define MOE_GEMM_CARRY 1
+#endif
 
 // Workgroup barrier for the tile pipeline.  __syncthreads() (and even an
 // LDS-scoped fence, since loads into LDS count as vector-memory operations)
@@ -407,6 +410,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float sw_cur = 0.f;   // weight-block scale of the current step (fused: gate)
+  // products of the most recent subtile row and their combined scales,
+  // promoted one row later (across the step boundary when kCarry)
+  constexpr bool kCarry = MOE_GEMM_CARRY != 0;
+  v4f tprev[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) tprev[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float fprev = 0.f, fprevu = 0.f;
   float swu_cur = 0.f;  // fused: up weight-block scale
 
   // One K step: A k-block kb in A stage SAi = kb % 3, B in B stage
@@ -459,11 +469,19 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
               sa_e[i]);
       }
     } else {
-    v4f tprev[NJ];
-    float fprev = 0.f, fprevu = 0.f;
+    // kCarry: the products of the last subtile row are promoted at the
+    // start of the next step (tprev and fprev persist across steps), so a
+    // wave reaches the step barrier right after issuing its last MFMA
+    // instead of waiting for it to finish.
+    if (!kCarry) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) tprev[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      fprev = fprevu = 0.f;
+    }
     v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
     for (int i = 0; i <= MI; ++i) {
+      if (kCarry && i == MI) break;
       v4f tcur[NJ];
       float fcur = 0.f, fcuru = 0.f;
       if (i < MI) {
@@ -474,14 +492,15 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(bf[j], af);
       }
-      if (i > 0) {
+      if (i > 0 || kCarry) {
+        const int ip = i > 0 ? i - 1 : MI - 1;   // row whose products are complete
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
-          acc[i - 1][j][0] = fmaf(tprev[j][0], f, acc[i - 1][j][0]);
-          acc[i - 1][j][1] = fmaf(tprev[j][1], f, acc[i - 1][j][1]);
-          acc[i - 1][j][2] = fmaf(tprev[j][2], f, acc[i - 1][j][2]);
-          acc[i - 1][j][3] = fmaf(tprev[j][3], f, acc[i - 1][j][3]);
+          acc[ip][j][0] = fmaf(tprev[j][0], f, acc[ip][j][0]);
+          acc[ip][j][1] = fmaf(tprev[j][1], f, acc[ip][j][1]);
+          acc[ip][j][2] = fmaf(tprev[j][2], f, acc[ip][j][2]);
+          acc[ip][j][3] = fmaf(tprev[j][3], f, acc[ip][j][3]);
         }
       }
       if (i < MI) {
@@ -538,6 +557,16 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     if (kb + 3 < Kb) step(kb + 3, I0(), I1());
     if (kb + 4 < Kb) step(kb + 4, I1(), I0());
     if (kb + 5 < Kb) step(kb + 5, I2(), I1());
+  }
+  if constexpr (kCarry && !kPow2) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
+      acc[MI - 1][j][0] = fmaf(tprev[j][0], f, acc[MI - 1][j][0]);
+      acc[MI - 1][j][1] = fmaf(tprev[j][1], f, acc[MI - 1][j][1]);
+      acc[MI - 1][j][2] = fmaf(tprev[j][2], f, acc[MI - 1][j][2]);
+      acc[MI - 1][j][3] = fmaf(tprev[j][3], f, acc[MI - 1][j][3]);
+    }
   }
 
   if constexpr (kFused) {
