@@ -186,7 +186,9 @@ def main():
                          "of the layer")
     ap.add_argument("--unfused", action="store_true",
                     help="run the gate/up GEMM and the activation as two calls "
-                         "(default: the layer's choice, fused at prefill sizes)")
+                         "(default: the layer's choice)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the gate/up GEMM with the activation fused (one call)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first "
                          "(reference for scaling HBM byte counters)")
@@ -246,7 +248,7 @@ def main():
     w_d = torch.from_numpy(w).to(dev)
     rows = cfg.capacity if cfg.layout == fre.LAYOUT_MASKED else fre.contiguous_rows(R, E, cfg.align_m)
     layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev,
-                         scale_fmt=args.scales, fuse_act=False if args.unfused else "auto")
+                         scale_fmt=args.scales, fuse_act=False if args.unfused else (True if args.fused else "auto"))
     fused = layer.fuse_act
     torch.cuda.synchronize()
 

@@ -14,10 +14,12 @@
 //   layout_scan    one block: per-chunk exclusive bases, counts, offsets
 //   layout_rank    one block per chunk: wave-ballot ranks in flat order,
 //                  writes slot_of, row_src, row_expert
-//   permute_rows   one wave per piece of a source row: reads x[t] once,
-//                  writes it to each of the token's slots (16-byte accesses)
-//   permute_scales the matching scales, 64 slots per workgroup transposed
-//                  through LDS (contiguous reads and stores)
+//   permute_kernel one launch of two kinds of workgroups:
+//                  scales: 64 slots per workgroup transposed through LDS
+//                  (contiguous reads and stores);
+//                  rows: one wave per piece of a source row, which reads
+//                  x[t] once and writes it to each of the token's slots
+//                  (16-byte accesses)
 #include "device_common.hpp"
 
 namespace moe {
@@ -243,11 +245,11 @@ constexpr int kPermChunks = MOE_PERM_CHUNKS;   // 16-byte chunks per lane
 // their piece in registers and store it to every slot of the token.  The
 // token's slots and the piece are requested together; only the stores wait
 // for the slots.
-__global__ __launch_bounds__(256) void permute_rows(
-    const uint8_t* __restrict__ x, const int32_t* __restrict__ slot_of, int T, int K, int H,
-    int pieces, int plen, int rows_total, uint8_t* __restrict__ a) {
+__device__ __forceinline__ void permute_rows(
+    int blk, const uint8_t* __restrict__ x, const int32_t* __restrict__ slot_of, int T, int K,
+    int H, int pieces, int plen, int rows_total, uint8_t* __restrict__ a) {
   const int lane = threadIdx.x & 63;
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long w = (long long)blk * 4 + (threadIdx.x >> 6);
   const long long t = w / pieces;
   if (t >= T) return;
   const int n16 = H >> 4;
@@ -283,12 +285,12 @@ __global__ __launch_bounds__(256) void permute_rows(
 // one block column, so both sides are contiguous runs.
 constexpr int kScTile = 64;
 
-__global__ __launch_bounds__(256) void permute_scales(
-    const uint32_t* __restrict__ x_scale, const int32_t* __restrict__ row_src, int T, int hb,
-    int rows_total, uint32_t* __restrict__ a_scale) {
+__device__ __forceinline__ void permute_scales(
+    int blk, const uint32_t* __restrict__ x_scale, const int32_t* __restrict__ row_src, int T,
+    int hb, int rows_total, uint32_t* __restrict__ a_scale) {
   __shared__ uint32_t tile[64][kScTile + 1];
   __shared__ int src_of[kScTile];
-  const int slot0 = blockIdx.x * kScTile;
+  const int slot0 = blk * kScTile;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (threadIdx.x < kScTile) {
     const int slot = slot0 + threadIdx.x;
@@ -310,6 +312,21 @@ __global__ __launch_bounds__(256) void permute_scales(
       if (live) a_scale[(long long)(kb0 + c) * rows_total + slot] = tile[c][lane];
     __syncthreads();
   }
+}
+
+// Rows and scales in one launch: the first scale_blocks workgroups permute
+// the scales (latency-bound, few bytes), the rest the rows (bandwidth-bound),
+// so the two overlap instead of running back to back.
+__global__ __launch_bounds__(256) void permute_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ slot_of, int T, int K, int H,
+    int pieces, int plen, int rows_total, uint8_t* __restrict__ a,
+    const uint32_t* __restrict__ x_scale, const int32_t* __restrict__ row_src, int hw,
+    uint32_t* __restrict__ a_scale, int scale_blocks) {
+  const int b = (int)blockIdx.x;
+  if (b < scale_blocks)
+    permute_scales(b, x_scale, row_src, T, hw, rows_total, a_scale);
+  else
+    permute_rows(b - scale_blocks, x, slot_of, T, K, H, pieces, plen, rows_total, a);
 }
 
 static int key_bits_for(int E) {
@@ -394,10 +411,12 @@ static moe_status_t dispatch(
     const int pieces = (n16 + 64 * kPermChunks - 1) / (64 * kPermChunks);
     const int plen = (n16 + pieces - 1) / pieces;
     const long long waves = (long long)T * pieces;
-    hipLaunchKernelGGL(permute_rows, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, x,
-                       slot_of, T, K, H, pieces, plen, (int)rows_total, a);
-    hipLaunchKernelGGL(permute_scales, dim3((unsigned)((rows_total + kScTile - 1) / kScTile)),
-                       dim3(256), 0, st, x_scale, row_src, T, hw, (int)rows_total, a_scale);
+    const long long row_blocks = (waves + 3) / 4;
+    const long long scale_blocks = (rows_total + kScTile - 1) / kScTile;
+    if (row_blocks + scale_blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
+    hipLaunchKernelGGL(permute_kernel, dim3((unsigned)(row_blocks + scale_blocks)), dim3(256),
+                       0, st, x, slot_of, T, K, H, pieces, plen, (int)rows_total, a, x_scale,
+                       row_src, hw, a_scale, (int)scale_blocks);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }

@@ -10,8 +10,9 @@ With fuse_act=False the gate/up GEMM and the activation run as two calls
 (moe_grouped_gemm_fp8 -> moe_act_requant) through a bf16 buffer h; both
 orders give the same q2 bit for bit.  fuse_act="auto" (the default) fuses
 when the library runs the gate/up GEMM with its large 256 x 256 tiles (the
-same size rule as the library's); at decode sizes the two calls measured
-faster (the fused kernel needs 128 x 256 tiles there, one workgroup per CU).
+same size rule as the library's); with the small tiles (the masked decode
+layout) the two calls measured faster, since the fused kernel then needs
+128 x 256 tiles at one workgroup per CU.
 
 All arithmetic happens in the HIP library; this class only holds memory.
 The call sequence allocates nothing and reads nothing back, so it can be
@@ -32,10 +33,12 @@ def contiguous_rows(R, E, align_m=128):
     return int(R) + E * (align_m - 1)
 
 
-def big_gate_up_tiles(rows_total, I):
+def big_gate_up_tiles(rows_total, I, E):
     """Whether the library runs the gate/up GEMM of this buffer with its
-    256 x 256 tiles: at least 512 full tiles (its host-side rule)."""
-    return (int(rows_total) // 256) * (2 * int(I) // 256) >= 512
+    256 x 256 tiles (its host-side rule): segments of 256 rows or more on
+    average and more than 128 such tiles."""
+    R, N = int(rows_total), 2 * int(I)
+    return N % 256 == 0 and R >= 256 * int(E) and (R // 256) * (N // 256) > 128
 
 
 class MoELayer:
@@ -52,7 +55,7 @@ class MoELayer:
         self.rows_total = E * rows if layout == ops.LAYOUT_MASKED else rows
         R, d = self.rows_total, device
         if fuse_act == "auto":
-            fuse_act = big_gate_up_tiles(R, I)
+            fuse_act = big_gate_up_tiles(R, I, E)
         self.fuse_act = bool(fuse_act)
         i32 = dict(dtype=torch.int32, device=d)
         self.counts = torch.zeros(E, **i32)
