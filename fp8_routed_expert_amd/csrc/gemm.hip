@@ -380,14 +380,28 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3"
                    : "=v"(fs_raw[c]) : "v"(base), "s"(rsrc_s), "n"(c * 256) : "memory");
   };
+  auto issue_a1 = [&](int kb, uint8_t* tA, int u) {
+    const int c = wave * CA + u;   // wave-uniform; parity of c is u's
+    dma16(rsrc_a, tA + c * 1024,
+          ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K +
+              (uint32_t)kb * kBK);
+  };
   auto issue_a = [&](int kb, uint8_t* tA) {
-    const uint32_t kofs = (uint32_t)kb * kBK;
 #pragma unroll
-    for (int u = 0; u < CA; ++u) {
-      const int c = wave * CA + u;   // wave-uniform; parity of c is u's
-      dma16(rsrc_a, tA + c * 1024,
-            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K + kofs);
-    }
+    for (int u = 0; u < CA; ++u) issue_a1(kb, tA, u);
+  };
+  // kLateA: the A rows of k-block kb + 2 are issued after the MFMAs of the
+  // first subtile row of step kb instead of with the B rows at its start.
+  // All waves issue their loads at once after the step barrier, and a wave
+  // stalls while the CU's address unit works through them; deferring the A
+  // half lets the first MFMAs start earlier.  Measured at the prefill shape:
+  // 0.6-1.9% off the unfused gate/up GEMM and the down GEMM over three boxes
+  // (deferring the B rows as well, or having only one wave per SIMD issue
+  // all the tile loads, was slower); the fused kernel keeps the early
+  // issue, with which it needs no register spills.
+  constexpr bool kLateA = !kFused;
+  auto issue_a_row = [&](int kb, uint8_t* tA, int i) {
+    if (i == 1) issue_a(kb, tA);   // MI >= 4
   };
   auto issue_b = [&](int kb, uint8_t* tB) {
     const uint32_t kofs = (uint32_t)kb * kBK;
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       issue_b(kb + 1, stB[(SBi + 1) % 2]);
       load_scales(kb + 1);
     }
-    if (ra) issue_a(kb + 2, stA[(SAi + 2) % 3]);
+    if (ra && !kLateA) issue_a(kb + 2, stA[(SAi + 2) % 3]);
     v8i bf[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bf[j] = load_frag(tB, wcol + j * 16 + r16, g);
@@ -460,6 +474,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
         const v8i af = af_next;
         if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
 #pragma unroll
@@ -485,6 +500,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       v4f tcur[NJ];
       float fcur = 0.f, fcuru = 0.f;
       if (i < MI) {
+        if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
         const v8i af = af_next;
         if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
         fcur = fs[i] * sw;

@@ -11,6 +11,7 @@ on the assembly hipcc produces for every GEMM kernel instance, that
     writes it when the load completes);
   * M0, which the DMA sequence sets, is not used by any compiler-generated
     instruction.
+  * no kernel spills registers to scratch memory.
 """
 
 import os
@@ -110,3 +111,11 @@ def test_m0_used_only_by_the_dma_sequence(kernels):
     for name, body in kernels.items():
         outside = [s for s, in_asm in body if re.search(r"\bm0\b", s) and not in_asm]
         assert not outside, (name, outside[:3])
+
+
+def test_no_register_spills(kernels):
+    """Every kernel instance fits its registers: a spill would put private
+    (scratch) memory traffic, and waits for it, into the K loop."""
+    for name, body in kernels.items():
+        spills = [s for s, _ in body if s.startswith("scratch_")]
+        assert not spills, (name, spills[:3])
