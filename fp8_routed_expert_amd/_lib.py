@@ -23,6 +23,7 @@ SIGNATURES = {
     "moe_abi_version": (_c_int, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "moe_layout_workspace_bytes": (_size, [_c_int, _c_int, _c_int]),
+    "moe_gemm_large_tiles": (_c_int, [ctypes.c_longlong, _c_int, _c_int]),
     "moe_dispatch_layout": (ctypes.c_int32, [
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
@@ -51,7 +52,7 @@ SIGNATURES = {
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 

@@ -803,6 +803,11 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
                                                     E, rows_total, N, K, c, st);
 }
 
+extern "C" int moe_gemm_large_tiles(long long rows_total, int N, int E) {
+  if (rows_total <= 0 || N <= 0 || E <= 0) return -1;
+  return use_big_tiles(rows_total, N, E) ? 1 : 0;
+}
+
 extern "C" moe_status_t moe_grouped_gemm_fp8(
     const uint8_t* a, const float* a_scale, const uint8_t* w,
     const float* w_scale, const int32_t* offsets, const int32_t* counts, int E,

@@ -35,10 +35,8 @@ def contiguous_rows(R, E, align_m=128):
 
 def big_gate_up_tiles(rows_total, I, E):
     """Whether the library runs the gate/up GEMM of this buffer with its
-    256 x 256 tiles (its host-side rule): segments of 256 rows or more on
-    average and more than 128 such tiles."""
-    R, N = int(rows_total), 2 * int(I)
-    return N % 256 == 0 and R >= 256 * int(E) and (R // 256) * (N // 256) > 128
+    256 x 256 tiles (asked from the library, which owns the rule)."""
+    return ops.moe_gemm_large_tiles(rows_total, 2 * int(I), E) == 1
 
 
 class MoELayer:

@@ -48,6 +48,12 @@ def moe_layout_workspace_bytes(T, K, E):
     return int(load().moe_layout_workspace_bytes(T, K, E))
 
 
+def moe_gemm_large_tiles(rows_total, N, E):
+    """1 if the GEMM calls run this size with 256 x 256 tiles, 0 if with the
+    small tiles, -1 for non-positive sizes (the library's host-side rule)."""
+    return int(load().moe_gemm_large_tiles(int(rows_total), int(N), int(E)))
+
+
 def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
                         offsets, slot_of, row_src, row_expert, a, a_scale,
                         workspace, status, stream=None):

@@ -101,3 +101,19 @@ def test_binding_refuses_host_tensors():
                         torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2),
                         torch.zeros(2, 128, dtype=torch.bfloat16),
                         torch.zeros(1, dtype=torch.int32))
+
+
+def test_gemm_tile_rule():
+    """The host-side tile choice that the layer's fuse rule relies on."""
+    lib = _lib.load()
+    f = lib.moe_gemm_large_tiles
+    assert f(132183, 4096, 9) == 1      # prefill EP32 share, gate/up
+    assert f(132183, 7168, 9) == 1      # and down
+    assert f(2556, 4096, 4) == 1        # EP72 decode share: 144 large tiles
+    assert f(6906, 4096, 6) == 1        # EP48 decode share
+    assert f(4096, 4096, 32) == 0       # masked, capacity 128: segments < 256 rows
+    assert f(636, 256, 4) == 0          # tiny
+    assert f(131072, 384, 1) == 0       # N not a multiple of 256
+    assert f(8192, 4096, 1) == 1        # dense, 32 x 16 large tiles
+    assert f(2048, 4096, 1) == 0        # dense, 8 x 16 = 128: not more than half the CUs
+    assert f(0, 4096, 1) == -1 and f(256, 0, 1) == -1 and f(256, 256, 0) == -1
