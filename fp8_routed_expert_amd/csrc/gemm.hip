@@ -75,9 +75,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
-#ifndef MOE_GEMM_CARRY
-#define MOE_GEMM_CARRY 1
-#endif
 
 // Workgroup barrier for the tile pipeline.  __syncthreads() (and even an
 // LDS-scoped fence, since loads into LDS count as vector-memory operations)
@@ -425,8 +422,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float sw_cur = 0.f;   // weight-block scale of the current step (fused: gate)
   // products of the most recent subtile row and their combined scales,
-  // promoted one row later (across the step boundary when kCarry)
-  constexpr bool kCarry = MOE_GEMM_CARRY != 0;
+  // promoted one row later, across the step boundary for the last row
   v4f tprev[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) tprev[j] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -484,48 +480,36 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
               sa_e[i]);
       }
     } else {
-    // kCarry: the products of the last subtile row are promoted at the
-    // start of the next step (tprev and fprev persist across steps), so a
-    // wave reaches the step barrier right after issuing its last MFMA
-    // instead of waiting for it to finish.
-    if (!kCarry) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) tprev[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-      fprev = fprevu = 0.f;
-    }
+    // The products of subtile row i are promoted while row i + 1 is
+    // multiplied, and those of the last row at the start of the next step
+    // (tprev and fprev persist across steps), so a wave reaches the step
+    // barrier right after issuing its last MFMA instead of waiting for it to
+    // finish.
     v8i af_next = load_frag(tA, wm * WM + r16, g);
 #pragma unroll
-    for (int i = 0; i <= MI; ++i) {
-      if (kCarry && i == MI) break;
+    for (int i = 0; i < MI; ++i) {
+      if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
+      const v8i af = af_next;
+      if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
+      const float fcur = fs[i] * sw;
+      const float fcuru = kFused ? fs[i] * swu : 0.f;
       v4f tcur[NJ];
-      float fcur = 0.f, fcuru = 0.f;
-      if (i < MI) {
-        if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
-        const v8i af = af_next;
-        if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
-        fcur = fs[i] * sw;
-        if (kFused) fcuru = fs[i] * swu;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(bf[j], af);
-      }
-      if (i > 0 || kCarry) {
-        const int ip = i > 0 ? i - 1 : MI - 1;   // row whose products are complete
+      for (int j = 0; j < NJ; ++j) tcur[j] = mfma_fp8_16x16x128(bf[j], af);
+      const int ip = i > 0 ? i - 1 : MI - 1;   // row whose products are complete
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
-          acc[ip][j][0] = fmaf(tprev[j][0], f, acc[ip][j][0]);
-          acc[ip][j][1] = fmaf(tprev[j][1], f, acc[ip][j][1]);
-          acc[ip][j][2] = fmaf(tprev[j][2], f, acc[ip][j][2]);
-          acc[ip][j][3] = fmaf(tprev[j][3], f, acc[ip][j][3]);
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
+        acc[ip][j][0] = fmaf(tprev[j][0], f, acc[ip][j][0]);
+        acc[ip][j][1] = fmaf(tprev[j][1], f, acc[ip][j][1]);
+        acc[ip][j][2] = fmaf(tprev[j][2], f, acc[ip][j][2]);
+        acc[ip][j][3] = fmaf(tprev[j][3], f, acc[ip][j][3]);
       }
-      if (i < MI) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
-        fprev = fcur;
-        fprevu = fcuru;
-      }
-      if (i > 0 && i < MI) {
+      for (int j = 0; j < NJ; ++j) tprev[j] = tcur[j];
+      fprev = fcur;
+      fprevu = fcuru;
+      if (i > 0) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -574,7 +558,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     if (kb + 4 < Kb) step(kb + 4, I1(), I0());
     if (kb + 5 < Kb) step(kb + 5, I2(), I1());
   }
-  if constexpr (kCarry && !kPow2) {
+  if constexpr (!kPow2) {   // the last row's products
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const float f = (kFused && j >= NJ / 2) ? fprevu : fprev;
