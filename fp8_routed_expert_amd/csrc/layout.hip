@@ -29,6 +29,7 @@ constexpr int kLayoutRounds = 4;
 constexpr int kChunk = kLayoutThreads * kLayoutRounds;   // flat entries per block
 constexpr int kWaves = kLayoutThreads / 64;
 constexpr int kScanThreads = 1024;
+constexpr long long kFoldMax = 8192;   // chunk x expert counts a rank block sums itself
 
 // Lanes of the wave whose key equals this lane's (ballots over the key bits).
 __device__ __forceinline__ unsigned long long match_key(int key, int key_bits) {
@@ -156,22 +157,76 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
 // group sizes go through LDS (tagged with the round so they never need
 // clearing) to order the four waves, and a running per-expert base carries
 // the count across rounds, so ranks follow flat order exactly.
+//
+// fold != 0 (few chunks, E <= kLayoutThreads): layout_scan is not launched.
+// Each block sums the chunk counts itself -- all of them for the expert
+// totals and segment starts, those of the earlier chunks for its own bases
+// -- and block 0 writes counts and offsets; the values equal layout_scan's.
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank(
     const int32_t* __restrict__ idx, long long F, int K, int E, int key_bits,
-    int layout, int rows_total, int cap, const int32_t* __restrict__ offsets,
+    int layout, int rows_total, int cap, int32_t* __restrict__ offsets,
     const int32_t* __restrict__ chunk_base, int32_t* __restrict__ slot_of,
     int32_t* __restrict__ row_src, int32_t* __restrict__ row_expert,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, int fold, const int32_t* __restrict__ chunk_counts,
+    int nchunks, int align_m, int32_t* __restrict__ counts) {
   extern __shared__ int32_t smem[];
   int32_t* run = smem;              // [E] running rank base
   int32_t* wcnt = smem + E;         // [kWaves][E] (round+1) << 8 | count
   int32_t* offs = wcnt + kWaves * E;  // [E] segment starts
+  int32_t* tot = offs + E;          // [E] expert totals (fold)
+  __shared__ long long wsum[kWaves];
   for (int i = threadIdx.x; i < E; i += blockDim.x) {
-    run[i] = chunk_base[(long long)blockIdx.x * E + i];
-    offs[i] = offsets[i];
+    if (fold) {
+      run[i] = 0;
+      tot[i] = 0;
+    } else {
+      run[i] = chunk_base[(long long)blockIdx.x * E + i];
+      offs[i] = offsets[i];
+    }
     for (int w = 0; w < kWaves; ++w) wcnt[w * E + i] = 0;
   }
   __syncthreads();
+  if (fold) {
+    // kLayoutThreads / E threads per expert, each summing a strided share of
+    // the chunks in registers, then one LDS add each
+    const int tpe = kLayoutThreads / E;
+    if ((int)threadIdx.x < tpe * E) {
+      const int e = threadIdx.x % E;
+      int sum = 0, before = 0;
+      for (int c = threadIdx.x / E; c < nchunks; c += tpe) {
+        const int v = chunk_counts[(long long)c * E + e];
+        sum += v;
+        if (c < (int)blockIdx.x) before += v;
+      }
+      atomicAdd(&tot[e], sum);
+      atomicAdd(&run[e], before);
+    }
+    __syncthreads();
+    // segment starts: exclusive scan over the experts (one per thread)
+    const int e = threadIdx.x;
+    long long mine = 0;
+    if (e < E)
+      mine = layout == MOE_LAYOUT_MASKED ? (long long)cap
+                                         : ((long long)tot[e] + align_m - 1) / align_m * align_m;
+    long long incl = mine;
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long v = __shfl_up(incl, d, 64);
+      if ((threadIdx.x & 63) >= d) incl += v;
+    }
+    if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) incl += wsum[w];
+    const long long lim = 0x7fffffffLL;
+    if (e < E) {
+      offs[e] = (int32_t)(incl - mine > lim ? lim : incl - mine);
+      if (blockIdx.x == 0) {
+        counts[e] = tot[e];
+        offsets[e] = offs[e];
+        if (e == E - 1) offsets[E] = (int32_t)(incl > lim ? lim : incl);
+      }
+    }
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -398,14 +453,17 @@ static moe_status_t dispatch(
   hipLaunchKernelGGL(layout_count, dim3((unsigned)ncl), dim3(kLayoutThreads),
                      E * sizeof(int32_t), st, topk_idx, F, E, key_bits_for(E), chunk_counts,
                      row_src, row_expert, (int)rows_total, status_dev);
-  hipLaunchKernelGGL(layout_scan, dim3(1), dim3(kScanThreads), 0, st, chunk_counts, ncl, E,
-                     scan_group(E), layout, align_m, cap, chunk_base, counts, offsets);
+  // few chunks: the rank blocks compute the scan themselves (one launch less)
+  const int fold = nc > 0 && E <= kLayoutThreads && nc * (long long)E <= kFoldMax;
+  if (!fold)
+    hipLaunchKernelGGL(layout_scan, dim3(1), dim3(kScanThreads), 0, st, chunk_counts, ncl, E,
+                       scan_group(E), layout, align_m, cap, chunk_base, counts, offsets);
   if (nc > 0)
     hipLaunchKernelGGL(layout_rank, dim3((unsigned)nc), dim3(kLayoutThreads),
-                       (2 + kWaves) * E * sizeof(int32_t), st, topk_idx, F, K,
+                       (3 + kWaves) * E * sizeof(int32_t), st, topk_idx, F, K,
                        E, key_bits_for(E), layout, (int)rows_total, cap,
                        offsets, chunk_base, slot_of, row_src, row_expert,
-                       status_dev);
+                       status_dev, fold, chunk_counts, ncl, align_m, counts);
   if (T > 0 && rows_total > 0) {
     const int n16 = H / 16;
     const int pieces = (n16 + 64 * kPermChunks - 1) / (64 * kPermChunks);
