@@ -12,6 +12,8 @@
 //   layout_count   one block per chunk of 1024 flat entries: LDS histogram
 //                  (ballot-grouped atomics); also row_src / row_expert <- -1
 //   layout_scan    one block: per-chunk exclusive bases, counts, offsets
+//                  (skipped when chunks x experts is small: layout_rank
+//                  then computes them itself)
 //   layout_rank    one block per chunk: wave-ballot ranks in flat order,
 //                  writes slot_of, row_src, row_expert
 //   permute_kernel one launch of two kinds of workgroups:
