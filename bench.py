@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=6144,
                     help="source tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
