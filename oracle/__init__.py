@@ -31,9 +31,13 @@ Modules:
   dense  - brute-force per-token dense MoE used only to pin `moe` on tiny
            inputs.
 
-Parity status: every function is pinned by a test under tests/ (exhaustive
-codec checks, closed forms, brute force, exact-integer GEMM cases).  No
-function here is "parity unpinned".
+Pins: every function is checked by a CPU test under tests/ against
+something other than itself -- exhaustive codec checks against torch's
+casts, the fp32 block quantiser against torch's fp32 ops, Python-loop brute
+force for the layout, permute and segment ranges, exact-integer and
+power-of-two-scale GEMM cases, closed forms for the activation and the
+combine, and a brute-force dense MoE for the whole layer (the test_oracle_*
+modules list which pin covers which function).
 """
 
 from . import codec, moe, dense  # noqa: F401

@@ -25,7 +25,7 @@ def _quant_expert(cfg, e):
     return q13, s13, q2, s2
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=6)
 def layer_inputs(cid, experts_needed_only=False):
     """Routing, quantised activations and weights of configuration `cid`.
 
@@ -81,7 +81,7 @@ def as_words(p):
     return np.ascontiguousarray(np.asarray(p, np.uint32).view(np.int32))
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=6)
 def layer_inputs_e8m0(cid, experts_needed_only=False):
     """layer_inputs with power-of-two scales (oracle.e8m0): for x, W13 and W2
     the codes, the exponents, the packed int32 words the device takes
@@ -89,7 +89,16 @@ def layer_inputs_e8m0(cid, experts_needed_only=False):
     ceil(I/512)]) and the fp32 scale values 2^e the oracle takes."""
     cfg = CONFIGS[cid]
     idx, w = routing(cfg)
-    x, xe = e8m0.quantize_blocks(bf16_to_f32(activations(cfg)), 1)
+    xb = activations(cfg)
+    x = np.empty((cfg.T, cfg.H), np.uint8)
+    xe = np.empty((cfg.T, cfg.H // 128), np.int32)
+    step = 4096
+
+    def qx(r0):
+        x[r0:r0 + step], xe[r0:r0 + step] = e8m0.quantize_blocks(
+            bf16_to_f32(xb[r0:r0 + step]), 1)
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(qx, range(0, cfg.T, step)))
     E, I, H = cfg.E, cfg.I, cfg.H
     w13 = np.zeros((E, 2 * I, H), np.uint8)
     e13 = np.zeros((E, 2 * I // 128, H // 128), np.int32)

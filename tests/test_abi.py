@@ -93,6 +93,35 @@ def test_host_argument_errors_launch_nothing():
     assert lib.moe_dispatch_layout(*a5) == 1
 
 
+def test_row_scale_span_limit():
+    """The row scales are addressed with 32-bit offsets: a call whose scale
+    array reaches 0x7ffff000 bytes is refused (MOE_UNSUPPORTED_SHAPE) before
+    any launch, in every GEMM entry point; one row less passes the check
+    and then fails on the null pointer it is given (INVALID_ARG)."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(4096)
+    K = 7168                                     # 56 scale blocks, 14 packed words
+    lim = 0x7ffff000
+    rows_f32 = lim // (56 * 4) + 1               # first row count over the limit
+    rows_e8 = lim // (14 * 4) + 1
+    assert lib.moe_grouped_gemm_fp8(fake, fake, fake, fake, fake, fake, 4, rows_f32, 4096, K,
+                                    fake, fake, N) == 2
+    assert lib.moe_grouped_gemm_fp8(fake, fake, fake, fake, N, fake, 4, rows_f32 - 1, 4096, K,
+                                    fake, fake, N) == 1
+    assert lib.moe_grouped_gemm_fp8_e8m0(fake, fake, fake, fake, fake, fake, 4, rows_e8, 4096,
+                                         K, fake, fake, N) == 2
+    assert lib.moe_grouped_gemm_fp8_e8m0(fake, fake, fake, fake, N, fake, 4, rows_e8 - 1,
+                                         4096, K, fake, fake, N) == 1
+    assert lib.moe_gate_up_act_fp8(fake, fake, fake, fake, fake, fake, 4, rows_f32, 2048, K,
+                                   fake, fake, fake, N) == 2
+    assert lib.moe_gate_up_act_fp8(fake, fake, fake, fake, N, fake, 4, rows_f32 - 1, 2048, K,
+                                   fake, fake, fake, N) == 1
+    assert lib.moe_gate_up_act_fp8_e8m0(fake, fake, fake, fake, fake, fake, 4, rows_e8, 2048,
+                                        K, fake, fake, fake, N) == 2
+    assert lib.moe_gemm_fp8(fake, fake, fake, fake, rows_f32, 4096, K, fake, N) == 2
+    assert lib.moe_gemm_fp8(fake, N, fake, fake, rows_f32 - 1, 4096, K, fake, N) == 1
+
+
 def test_binding_refuses_host_tensors():
     import torch
     import fp8_routed_expert_amd as fre

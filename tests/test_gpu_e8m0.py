@@ -10,14 +10,12 @@ import torch
 import fp8_routed_expert_amd as fre
 from oracle import moe, e8m0
 from oracle.codec import e4m3_encode, bf16_decode
-from tests.gpu_util import dev, host, bf16_vals, check_close, code_agreement, log
+from tests import chained
+from tests.gpu_util import dev, host, check_close, code_agreement, log
 from tests.inputs import layer_inputs_e8m0, rows_for, as_words
 from workloads import bf16_to_f32
 
 pytestmark = pytest.mark.gpu
-
-CHAINED_REL_L2 = 3e-3
-
 
 def _bf16(g, shape, scale_spread=6.0):
     x = g.standard_normal(shape) * np.exp(g.uniform(-scale_spread, scale_spread, (shape[0], 1)))
@@ -96,7 +94,10 @@ def test_gemm_e8m0_exact_integers(gpu):
             assert np.array_equal(bf16_decode(got[s:en]), ref), e
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
+ALL = [1, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("cid", ALL)
 def test_gemm1_e8m0_parity(gpu, cid):
     inp = layer_inputs_e8m0(cid, experts_needed_only=True)
     cfg = inp["cfg"]
@@ -117,6 +118,40 @@ def test_gemm1_e8m0_parity(gpu, cid):
         ref[sel] = moe.gemm_rows(a[rs[sel]], e8m0.scales(ea[rs[sel]]), inp["w13"][e],
                                  inp["s13"][e])
     check_close(bf16_decode(got[rs]), ref, f"gemm1 e8m0 config {cid} ({len(rs)} rows)")
+
+
+@pytest.mark.parametrize("cid", ALL)
+def test_gemm2_e8m0_parity(gpu, cid):
+    """Stage-isolated down projection with packed power-of-two scales:
+    oracle-quantised (R18-R19) rows on sampled slots of every expert,
+    including each segment's first and last row, against oracle.moe.gemm_rows
+    fed the scales 2^e."""
+    inp = layer_inputs_e8m0(cid, experts_needed_only=True)
+    cfg = inp["cfg"]
+    rows = rows_for(cfg, inp["idx"])
+    kw = dict(capacity=rows) if cfg.layout == moe.LAYOUT_MASKED else \
+        dict(align_m=cfg.align_m, rows=rows)
+    L = moe.dispatch_layout(inp["idx"], cfg.E, cfg.layout, **kw)
+    R = L["rows_total"]
+    g = np.random.default_rng(100 + cid)
+    rs = set()
+    for s, en in moe.expert_segments(L):
+        if en > s:
+            rs |= {s, en - 1}
+            rs |= set(g.choice(np.arange(s, en), size=min(6, en - s), replace=False).tolist())
+    rs = np.array(sorted(rs))
+    q2 = np.zeros((R, cfg.I), np.uint8)
+    eq = np.zeros((R, cfg.I // 128), np.int32)
+    vals = g.standard_normal((len(rs), cfg.I)) * np.exp(g.uniform(-3, 3, (len(rs), 1)))
+    q2[rs], eq[rs] = e8m0.quantize_blocks(vals, 1)
+    got = _run_gemm_e8m0(q2, eq, inp["w2"], inp["e2"], L["offsets"], L["counts"])
+    ex = L["row_expert"][rs]
+    ref = np.zeros((len(rs), cfg.H))
+    for e in np.unique(ex):
+        sel = ex == e
+        ref[sel] = moe.gemm_rows(q2[rs[sel]], e8m0.scales(eq[rs[sel]]), inp["w2"][e],
+                                 inp["s2"][e])
+    check_close(bf16_decode(got[rs]), ref, f"gemm2 e8m0 config {cid} ({len(rs)} rows)")
 
 
 def test_act_e8m0_vs_oracle(gpu):
@@ -147,33 +182,31 @@ def test_act_e8m0_vs_oracle(gpu):
     assert np.all(pad == 0x7F7F7F)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
-def test_layer_e8m0_chained(gpu, cid):
-    inp = layer_inputs_e8m0(cid, experts_needed_only=True)
-    cfg = inp["cfg"]
-    rows = rows_for(cfg, inp["idx"])
-    # the unfused order, so that h is checked too; the fused call gives the
-    # same q2 bit for bit (tests/test_gpu_fused.py)
-    layer = fre.MoELayer(cfg.E, cfg.H, cfg.I, cfg.T, cfg.K, cfg.layout, rows,
-                         align_m=cfg.align_m, scale_fmt="e8m0", fuse_act=False)
-    layer.status.zero_()
-    layer.forward(dev(inp["idx"]), dev(inp["x"]), dev(inp["xp"]), dev(inp["w"]),
-                  dev(inp["w13"]), dev(inp["p13"]), dev(inp["w2"]), dev(inp["p2"]))
-    torch.cuda.synchronize()
-    assert int(host(layer.status)[0]) == 0
-    kw = dict(capacity=rows) if cfg.layout == moe.LAYOUT_MASKED else \
-        dict(align_m=cfg.align_m, rows=rows)
-    T = cfg.T
-    toks = np.arange(T) if T <= 64 else np.sort(np.random.default_rng(cid).choice(T, 24, replace=False))
-    log(f"e8m0 config {cid}: oracle on {len(toks)} tokens")
-    ref = moe.layer(inp["x"], inp["xs"], inp["idx"], inp["w"], inp["w13"], inp["s13"],
-                    inp["w2"], inp["s2"], cfg.layout, tokens=toks, requant=e8m0.act_requant, **kw)
-    slots = ref["slots"]
-    check_close(bf16_vals(layer.h)[slots], ref["h"], f"e8m0 config {cid} h")
-    # chained codes are decided from the device's own h (see the fp32-scale
-    # chained test for the size of that difference)
-    code_agreement(host(layer.q2)[slots], ref["q2"], f"e8m0 config {cid} q2", minimum=0.995)
-    check_close(bf16_vals(layer.y)[slots], ref["y"], f"e8m0 config {cid} y",
-                rel_l2_tol=CHAINED_REL_L2)
-    out = bf16_vals(layer.out)
-    check_close(out[toks], ref["out"], f"e8m0 config {cid} out", rel_l2_tol=CHAINED_REL_L2)
+def _acceptance_params(cids):
+    ps = []
+    for cid in cids:
+        for fuse in (True, False):
+            reason = chained.known_miss_reason("e8m0", cid)
+            marks = [pytest.mark.xfail(strict=True, reason=reason)] if reason else []
+            ps.append(pytest.param(cid, fuse, marks=marks,
+                                   id=f"{cid}-{'fused' if fuse else 'unfused'}"))
+    return ps
+
+
+@pytest.mark.parametrize("cid,fuse", _acceptance_params(ALL))
+def test_layer_e8m0_chained(gpu, cid, fuse):
+    """The packed-scale layer against the oracle's packed-scale chain at the
+    workload's acceptance bars; recorded misses are strict expected failures
+    carrying their measured numbers (tests/chained.py)."""
+    res = chained.chained("e8m0", cid, fuse)
+    chained.check_hard(res)
+    chained.check_acceptance(res)
+
+
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused", "unfused"])
+@pytest.mark.parametrize("cid", ALL)
+def test_layer_e8m0_chained_no_regression(gpu, cid, fuse):
+    """Regression guard, not the acceptance bar (see the fp32-scale one)."""
+    res = chained.chained("e8m0", cid, fuse)
+    chained.check_hard(res)
+    chained.check_regression("e8m0", cid, res)

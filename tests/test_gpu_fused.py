@@ -56,7 +56,7 @@ def _assert_same(qu, su, qf, sf, valid, what):
     log(f"{what}: {int(valid.sum())} valid rows bit-identical")
 
 
-CASES = [(c, "fp32") for c in (1, 2, 3, 4, 5)] + [(c, "e8m0") for c in (1, 2, 5)]
+CASES = [(c, fmt) for fmt in ("fp32", "e8m0") for c in (1, 2, 3, 4, 5)]
 
 
 @pytest.mark.parametrize("cid,fmt", CASES, ids=lambda v: str(v))

@@ -7,13 +7,13 @@ import torch
 
 import fp8_routed_expert_amd as fre
 from oracle import moe
-from tests.gpu_util import dev, host, bf16_vals, check_close, code_agreement, log
+from tests import chained
+from tests.gpu_util import dev, host
 from tests.inputs import layer_inputs, rows_for
 
 pytestmark = pytest.mark.gpu
 
 ALL = [1, 2, 3, 4, 5]
-CHAINED_REL_L2 = 3e-3
 
 
 class DeviceInputs:
@@ -38,69 +38,39 @@ def _layer(cfg, rows, layout=None, fuse_act=True):
                         fuse_act=fuse_act)
 
 
-def _sample_tokens(inp, L, n=24, seed=0):
-    """Tokens with the most rows, tokens owning segment boundary rows, and
-    random tokens (all tokens for the tiny configuration)."""
-    T = inp["idx"].shape[0]
-    if T <= 64:
-        return np.arange(T)
-    g = np.random.default_rng(seed)
-    nrows = (inp["idx"] >= 0).sum(1)
-    picks = set(np.argsort(-nrows, kind="stable")[:4].tolist())
-    for s, en in moe.expert_segments(L):
-        if en > s:
-            picks.add(int(L["row_src"][s]))
-            picks.add(int(L["row_src"][en - 1]))
-    picks |= set(g.choice(T, size=n, replace=False).tolist())
-    picks.add(int(np.argmin(nrows)))
-    return np.array(sorted(picks))
+def _acceptance_params(fmt, cids):
+    ps = []
+    for cid in cids:
+        for fuse in (True, False):
+            reason = chained.known_miss_reason(fmt, cid)
+            marks = [pytest.mark.xfail(strict=True, reason=reason)] if reason else []
+            ps.append(pytest.param(cid, fuse, marks=marks,
+                                   id=f"{cid}-{'fused' if fuse else 'unfused'}"))
+    return ps
+
+
+@pytest.mark.parametrize("cid,fuse", _acceptance_params("fp32", ALL))
+def test_layer_chained_parity(gpu, cid, fuse):
+    """The whole layer against the oracle at the workload's acceptance bars
+    (q2 codes >= 99.9%, y and out rel L2 <= 2e-3, per-element bound).
+    fused: gate/up GEMM and activation in one call (the default layer at
+    large sizes); unfused: two calls through the bf16 buffer h.  A
+    configuration recorded as missing a bar is a strict expected failure
+    whose reason carries the measured numbers (tests/chained.py)."""
+    res = chained.chained("fp32", cid, fuse)
+    chained.check_hard(res)
+    chained.check_acceptance(res)
 
 
 @pytest.mark.parametrize("fuse", [True, False], ids=["fused", "unfused"])
 @pytest.mark.parametrize("cid", ALL)
-def test_layer_chained_parity(gpu, cid, fuse):
-    """The whole layer against the oracle; fused: gate/up GEMM and
-    activation in one call (the default layer), unfused: two calls through
-    the bf16 buffer h, which is then checked too."""
-    inp = layer_inputs(cid, experts_needed_only=True)
-    cfg = inp["cfg"]
-    rows = rows_for(cfg, inp["idx"])
-    layer = _layer(cfg, rows, fuse_act=fuse)
-    d = DeviceInputs(inp)
-    layer.status.zero_()
-    d.run(layer)
-    torch.cuda.synchronize()
-    assert int(host(layer.status)[0]) == 0
-    kw = dict(capacity=rows) if cfg.layout == moe.LAYOUT_MASKED else \
-        dict(align_m=cfg.align_m, rows=rows)
-    L = moe.dispatch_layout(inp["idx"], cfg.E, cfg.layout, **kw)
-    toks = _sample_tokens(inp, L)
-    log(f"config {cid}: oracle on {len(toks)} tokens")
-    ref = moe.layer(inp["x"], inp["xs"], inp["idx"], inp["w"], inp["w13"], inp["s13"],
-                    inp["w2"], inp["s2"], cfg.layout, tokens=toks, **kw)
-    slots = ref["slots"]
-    assert np.array_equal(host(layer.slot_of), ref["layout"]["slot_of"])
-    if not fuse:
-        check_close(bf16_vals(layer.h)[slots], ref["h"], f"config {cid} h")
-    # q2 codes here are decided from the device's own h, which differs from
-    # the oracle's correctly rounded bf16 h by one ulp in ~1.2% of elements
-    # (the FP8 matrix-core sum of 128 products carries an error of ~1e-6 of
-    # the sum of |products|); a one-ulp change of a block's amax moves the
-    # whole block's scale, so chained codes are held to 99.5% while the
-    # 99.9% bar applies where both sides decide from the same h (stage test).
-    code_agreement(host(layer.q2)[slots], ref["q2"], f"config {cid} q2", minimum=0.995)
-    # The same one-ulp h differences move some blocks' q2 scales by ~0.4%,
-    # which shifts every dequantised value of such a block; chained y and out
-    # therefore carry ~1.5-2.2e-3 relative L2 against the exact oracle
-    # (measured on all five workloads) and are held to 3e-3 here, while every
-    # stage-isolated output (tests/test_gpu_stages.py) is held to 2e-3.  The
-    # per-element bound (0.02 * max|ref|) is unchanged.
-    check_close(bf16_vals(layer.y)[slots], ref["y"], f"config {cid} y", rel_l2_tol=CHAINED_REL_L2)
-    out = bf16_vals(layer.out)
-    check_close(out[toks], ref["out"], f"config {cid} out", rel_l2_tol=CHAINED_REL_L2)
-    # every token with no routed row is exactly zero
-    empty = (inp["idx"] < 0).all(axis=1)
-    assert np.all(out[empty] == 0)
+def test_layer_chained_no_regression(gpu, cid, fuse):
+    """Regression guard, not the acceptance bar: layout bit-exact, status
+    clear, per-element bounds, h within the stage bar, and chained metrics
+    no worse than the MI355X record."""
+    res = chained.chained("fp32", cid, fuse)
+    chained.check_hard(res)
+    chained.check_regression("fp32", cid, res)
 
 
 @pytest.mark.parametrize("fuse", [True, False], ids=["fused", "unfused"])

@@ -263,6 +263,64 @@ def test_gemm_exact_integers_pow2_scales(gpu):
             assert np.array_equal(bf16_decode(got[s:en]), ref), e
 
 
+CORRUPT_TABLES = [
+    ("decreasing", [0, 100, 90, 220], [100, 50, 70]),      # expert 2 starts inside expert 1
+    ("negative_count", [0, 100, 150, 220], [100, -5, 70]),
+    ("negative_start", [-64, 100, 150, 220], [100, 50, 70]),
+]
+
+
+@pytest.mark.parametrize("name,offs,cnts", CORRUPT_TABLES, ids=[c[0] for c in CORRUPT_TABLES])
+def test_corrupt_segment_table_flagged(gpu, name, offs, cnts):
+    """A segment table that does not describe segments sets
+    MOE_ERR_BAD_INDEX in the gate/up GEMM, the activation and the fused
+    call; rows of segments the table still describes correctly come out
+    exactly as with the good table, and nothing outside the buffer is
+    touched (every row index is clipped)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    E, I, H, rows = 3, 128, 256, 256
+    good_o = np.array([0, 100, 150, 220], np.int32)
+    good_c = np.array([100, 50, 70], np.int32)
+    a = torch.randint(0, 0x7E, (rows, H), dtype=torch.uint8, device="cuda", generator=g)
+    sa = torch.rand(H // 128, rows, device="cuda", generator=g) + 0.5
+    w = torch.randint(0, 0x7E, (E, 2 * I, H), dtype=torch.uint8, device="cuda", generator=g)
+    sw = torch.rand(E, 2 * I // 128, H // 128, device="cuda", generator=g) * 1e-3
+
+    def run(o, c):
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        od, cd = dev(np.array(o, np.int32)), dev(np.array(c, np.int32))
+        h = torch.zeros(rows, 2 * I, dtype=torch.bfloat16, device="cuda")
+        q = torch.zeros(rows, I, dtype=torch.uint8, device="cuda")
+        qs = torch.zeros(I // 128, rows, dtype=torch.float32, device="cuda")
+        qf, qfs = q.clone(), qs.clone()
+        fre.moe_grouped_gemm_fp8(a, sa, w, sw, od, cd, h, st)
+        torch.cuda.synchronize()
+        st_gemm = int(host(st)[0])
+        st.zero_()
+        fre.moe_act_requant(h, od, cd, q, qs, st)
+        torch.cuda.synchronize()
+        st_act = int(host(st)[0])
+        st.zero_()
+        fre.moe_gate_up_act_fp8(a, sa, w, sw, od, cd, qf, qfs, st)
+        torch.cuda.synchronize()
+        st_fused = int(host(st)[0])
+        return (st_gemm, st_act, st_fused), host(h), host(q), host(qs), host(qf), host(qfs)
+
+    sg, h0, q0, qs0, qf0, qfs0 = run(good_o, good_c)
+    assert sg == (0, 0, 0)
+    sb, h1, q1, qs1, qf1, qfs1 = run(offs, cnts)
+    assert all(v == fre.ERR_BAD_INDEX for v in sb), sb
+    # rows described identically by both tables and written by no other
+    # segment: expert 0's (in "decreasing", expert 2's segment [90, 160)
+    # overlaps its last ten rows), or expert 1's when expert 0's start is bad
+    keep = {"decreasing": slice(0, 90), "negative_count": slice(0, 100),
+            "negative_start": slice(100, 150)}[name]
+    assert np.array_equal(h1[keep], h0[keep])
+    assert np.array_equal(q1[keep], q0[keep]) and np.array_equal(qs1[:, keep], qs0[:, keep])
+    assert np.array_equal(qf1[keep], qf0[keep]) and np.array_equal(qfs1[:, keep], qfs0[:, keep])
+
+
 def test_gemm_exact_many_experts(gpu):
     """More experts than one wave has lanes (the tile lookup then takes
     several passes of 64 experts): 150 experts, a third of them empty, the

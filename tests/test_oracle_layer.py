@@ -275,3 +275,171 @@ def test_layer_token_subset_matches_full():
     toks = np.array([3, 17, 40, 63])
     sub = moe.layer(x, xs, idx, w, w13, s13, w2, s2, C, align_m=128, rows=1024, tokens=toks)
     assert np.array_equal(sub["out"], full["out"][toks])
+
+
+# ------------------------------------------------------------------ R4 against torch
+def _torch_fp32_quantiser(v, block_rows):
+    """An independent fp32 block quantiser built from torch CPU primitives:
+    amax and amax / 448 in fp32, unit scale for an all-zero block, then
+    (v / s) saturated to +-448 and cast by torch's float8_e4m3fn conversion
+    (round to nearest even).  Shares nothing with oracle.codec."""
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
+    R, Cn = x.shape
+    blk = x.reshape(R // block_rows, block_rows, Cn // 128, 128)
+    amax = blk.abs().amax(dim=(1, 3))
+    s = amax / torch.tensor(448.0, dtype=torch.float32)
+    s = torch.where(amax == 0, torch.ones_like(s), s)
+    quot = blk / s[:, None, :, None]
+    q = quot.clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(R, Cn).numpy(), s.numpy()
+
+
+def _tie_heavy_bf16(g, rows):
+    """bf16 rows whose block scale is an exact power of two (each block holds
+    +-448 * 2^k) and whose other values sit exactly on E4M3 rounding
+    midpoints (5 significant bits, so bf16-exact), or one bf16 ulp beside
+    them: every code is decided by the tie rule or by one ulp."""
+    from oracle.codec import e4m3_decode as dec
+    vals = np.unique(np.abs(dec(np.arange(0x7F))))
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    out = np.empty((rows, 256), np.float32)
+    for r in range(rows):
+        for b in range(2):
+            k = int(g.integers(-20, 20))
+            m = g.choice(mids, size=128) * np.where(g.random(128) < 0.5, -1.0, 1.0)
+            m = m.astype(np.float32)
+            nudge = g.integers(-1, 2, size=128).astype(np.int32)   # -1, 0, +1 ulp
+            bits = m.view(np.uint32).astype(np.int64) + (nudge << 16)
+            m = (bits.astype(np.uint32)).view(np.float32)
+            m[int(g.integers(0, 128))] = 448.0 * (1 if g.random() < 0.5 else -1)
+            out[r, b * 128:(b + 1) * 128] = np.ldexp(m, k)
+    return out
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_quantize_blocks_r4_matches_torch_fp32_quantiser(block_rows):
+    """R4 (codes decided from the correctly rounded fp32 quotient v / s) is
+    the conventional fp32 quantiser; torch's CPU ops compute the same thing
+    independently.  Random bf16 blocks over a wide dynamic range, tie-heavy
+    blocks, zero blocks and subnormal-range blocks: codes and scales bit-exact."""
+    g = np.random.default_rng(20 + block_rows)
+    R = 256 if block_rows == 1 else 384
+    v = (g.standard_normal((R, 512)) *
+         np.exp(g.uniform(-30, 30, (R // block_rows, 1))).repeat(block_rows, 0))
+    v = bf16_to_f32(_bf16_bits(v))
+    v[:block_rows, :128] = 0.0                                     # zero block
+    v[block_rows:2 * block_rows, 128:256] *= 2.0 ** -120           # tiny scales
+    q, s = moe.quantize_blocks(v, block_rows)
+    tq, ts = _torch_fp32_quantiser(v, block_rows)
+    assert np.array_equal(s, ts)
+    assert np.array_equal(q, tq)
+    if block_rows == 1:
+        t = _tie_heavy_bf16(g, 64)
+        q, s = moe.quantize_blocks(t, 1)
+        tq, ts = _torch_fp32_quantiser(t, 1)
+        assert np.array_equal(s, ts) and np.array_equal(q, tq)
+        # the blocks really are tie-heavy: about a third of the quotients
+        # lie exactly on a rounding midpoint
+        from oracle.codec import e4m3_decode as dec
+        vals = np.unique(np.abs(dec(np.arange(0x7F))))
+        mids = set(((vals[:-1] + vals[1:]) / 2.0).tolist())
+        quot = np.abs(t / np.repeat(s, 128, axis=1)).astype(np.float64).ravel()
+        assert np.mean([x in mids for x in quot]) > 0.25
+
+
+def _bf16_bits(a):
+    import torch
+    return (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+            .view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------------ permute / segments
+def _distinct_rows(g, T, H):
+    """Source rows that differ from each other in every 16-byte piece (the
+    token id is written into each piece), so any row or piece moved to the
+    wrong slot is caught."""
+    x = g.integers(0, 256, size=(T, H), dtype=np.uint8)
+    for p in range(0, H, 16):
+        x[:, p] = np.arange(T) & 0xFF
+        x[:, p + 1] = (np.arange(T) >> 8) & 0xFF
+    xs = g.standard_normal((T, H // 128)).astype(np.float32)
+    xs[:, 0] = np.arange(T, dtype=np.float32)
+    return x, xs
+
+
+@pytest.mark.parametrize("case", ["contig", "contig_overflow", "masked_drops", "bad_ids"])
+def test_permute_vs_brute(case):
+    """moe.permute against a walk over (t, k) in the Python-loop layout:
+    every routed, kept entry's slot holds its token's row and scales byte for
+    byte; every other slot is zero and reported unfilled."""
+    g = np.random.default_rng(7)
+    T, K, E, H = 90, 4, 5, 384
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        n = int(g.integers(0, K + 1))
+        idx[t, g.permutation(K)[:n]] = g.permutation(E)[:n]
+    kw = dict(align_m=8, rows=T * K + E * 8)
+    layout = C
+    if case == "contig_overflow":
+        kw = dict(align_m=8, rows=100)
+    elif case == "masked_drops":
+        layout, kw = M, dict(capacity=12)
+    elif case == "bad_ids":
+        idx[g.random((T, K)) < 0.1] = 9
+        idx[g.random((T, K)) < 0.05] = -4
+    x, xs = _distinct_rows(g, T, H)
+    L = moe.dispatch_layout(idx, E, layout, **kw)
+    a, sa, filled = moe.permute(x, xs, L)
+    _, _, slot_of, _, _, _ = brute_layout(idx, E, layout, **kw)
+    rows_total = L["rows_total"]
+    want_a = np.zeros((rows_total, H), np.uint8)
+    want_s = np.zeros((rows_total, H // 128), np.float32)
+    want_f = np.zeros(rows_total, bool)
+    for t in range(T):
+        for k in range(K):
+            s = slot_of[t][k]
+            if s >= 0:
+                assert not want_f[s]            # a slot is filled once
+                want_a[s], want_s[s], want_f[s] = x[t], xs[t], True
+    assert np.array_equal(filled, want_f)
+    assert np.array_equal(a, want_a)
+    assert np.array_equal(sa, want_s)
+    assert want_f.sum() == sum(s >= 0 for row in slot_of for s in row)
+
+
+@pytest.mark.parametrize("case", ["contig", "contig_overflow", "masked_drops", "empty_experts"])
+def test_expert_segments_vs_brute(case):
+    """moe.expert_segments against the slots the Python-loop layout actually
+    filled for each expert: a segment is exactly [first, last + 1) of the
+    expert's filled slots, it starts at the expert's offset (clipped to the
+    buffer), and an expert with no kept row has an empty segment there."""
+    g = np.random.default_rng(8)
+    T, K, E = 120, 3, 6
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        n = int(g.integers(1, K + 1))
+        idx[t, g.permutation(K)[:n]] = g.permutation(E)[:n]
+    layout, kw = C, dict(align_m=16, rows=T * K + E * 16)
+    if case == "contig_overflow":
+        kw = dict(align_m=16, rows=150)
+    elif case == "masked_drops":
+        layout, kw = M, dict(capacity=20)
+    elif case == "empty_experts":
+        idx[(idx == 1) | (idx == 4)] = -1
+    L = moe.dispatch_layout(idx, E, layout, **kw)
+    counts, offsets, slot_of, row_src, row_exp, _ = brute_layout(idx, E, layout, **kw)
+    rows_total = kw["rows"] if layout == C else E * kw["capacity"]
+    segs = moe.expert_segments(L)
+    assert len(segs) == E
+    for e in range(E):
+        mine = [s for s in range(rows_total) if row_exp[s] == e]
+        s0, s1 = segs[e]
+        if mine:
+            assert (s0, s1) == (min(mine), max(mine) + 1)
+            assert mine == list(range(s0, s1))      # contiguous, no gaps
+            assert s0 == offsets[e]
+        else:
+            assert s0 == s1 == min(offsets[e], rows_total)
+    if case == "empty_experts":
+        assert segs[1][0] == segs[1][1] and segs[4][0] == segs[4][1]

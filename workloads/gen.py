@@ -183,10 +183,12 @@ def _bf16(a):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def activations(cfg):
-    """x ~ N(0, 1) as bf16 bits [T, H]."""
+def activations(cfg, first_rows=None):
+    """x ~ N(0, 1) as bf16 bits [T, H] (or only its first `first_rows` rows,
+    which are the same values: the stream is drawn row by row)."""
     g = rng(cfg.cid, STREAM_X)
-    return _bf16(g.standard_normal((cfg.T, cfg.H), dtype=np.float32))
+    n = cfg.T if first_rows is None else min(int(first_rows), cfg.T)
+    return _bf16(g.standard_normal((n, cfg.H), dtype=np.float32))
 
 
 def weights(cfg, experts=None):
