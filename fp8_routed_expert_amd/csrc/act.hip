@@ -38,8 +38,13 @@ template <bool kPow2>
 __global__ __launch_bounds__(kActThreads) void act_requant_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int E, int rows_total, int I,
-    uint8_t* __restrict__ q, void* __restrict__ q_scale) {
+    uint8_t* __restrict__ q, void* __restrict__ q_scale, int32_t* __restrict__ status) {
   const int m = blockIdx.x;
+  // the first workgroup's first wave checks that offsets / counts describe
+  // segments (rows are clipped to the buffer whatever they hold)
+  if (m == 0 && blockIdx.y == 0 && threadIdx.x < 64 && status &&
+      segments_bad(offsets, counts, E, threadIdx.x) && threadIdx.x == 0)
+    atomicOr(status, MOE_ERR_BAD_INDEX);
   const int j0 = blockIdx.y * kActCols + threadIdx.x * 8;
   const bool in_row = j0 < I;
   const uint16_t* hrow = h + (size_t)m * 2 * I;
@@ -83,7 +88,7 @@ using namespace moe;
 template <bool kPow2>
 static moe_status_t act_requant(const uint16_t* h, const int32_t* offsets,
                                 const int32_t* counts, int E, int rows_total, int I,
-                                uint8_t* q, void* q_scale, void* stream) {
+                                uint8_t* q, void* q_scale, int32_t* status, void* stream) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0) return MOE_INVALID_ARG;
   if (I % kBlock != 0) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts) return MOE_INVALID_ARG;
@@ -94,7 +99,7 @@ static moe_status_t act_requant(const uint16_t* h, const int32_t* offsets,
   hipLaunchKernelGGL((act_requant_kernel<kPow2>),
                      dim3((unsigned)rows_total, (unsigned)((I + kActCols - 1) / kActCols)),
                      dim3(kActThreads), 0, st, h, offsets, counts, E, rows_total, I, q,
-                     q_scale);
+                     q_scale, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
@@ -102,14 +107,14 @@ extern "C" moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offset
                                         const int32_t* counts, int E, int rows_total,
                                         int I, uint8_t* q, float* q_scale,
                                         int32_t* status_dev, void* stream) {
-  (void)status_dev;
-  return act_requant<false>(h, offsets, counts, E, rows_total, I, q, q_scale, stream);
+  return act_requant<false>(h, offsets, counts, E, rows_total, I, q, q_scale, status_dev,
+                            stream);
 }
 
 extern "C" moe_status_t moe_act_requant_e8m0(const uint16_t* h, const int32_t* offsets,
                                              const int32_t* counts, int E, int rows_total,
                                              int I, uint8_t* q, uint32_t* q_scale,
                                              int32_t* status_dev, void* stream) {
-  (void)status_dev;
-  return act_requant<true>(h, offsets, counts, E, rows_total, I, q, q_scale, stream);
+  return act_requant<true>(h, offsets, counts, E, rows_total, I, q, q_scale, status_dev,
+                           stream);
 }

@@ -133,8 +133,9 @@ __device__ __forceinline__ uint32_t requant8(const float v[8], float amax, uint2
 }
 
 // Valid row range of expert e: [start, end) inside the segment and buffer.
-// Returns false (and flags) when the segment description is outside the
-// buffer; the range is then clipped so callers never index out of bounds.
+// Whatever offsets and counts hold, the range is clipped to the buffer, so
+// callers never index out of bounds (segments_bad() below detects a table
+// that does not describe segments).
 __device__ __forceinline__ void expert_rows(const int32_t* offsets,
                                             const int32_t* counts, int e,
                                             int rows_total, int& start,
@@ -150,6 +151,25 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets,
   if (lim < s) lim = s;
   start = (int)s;
   end = (int)lim;
+}
+
+// Does the segment table fail to describe segments?  True when a start is
+// negative, the starts decrease, or a count is negative, for any expert
+// handled by this wave (expert base + lane, for base = 0, 64, ...).  A
+// segment that reaches past the buffer end is not flagged: that is the
+// overflow case of the layout, flagged by the dispatch, and is clipped.
+// Wave-uniform result.
+__device__ __forceinline__ bool segments_bad(const int32_t* offsets, const int32_t* counts,
+                                             int E, int lane) {
+  bool bad = false;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    if (e < E) {
+      const int o0 = offsets[e], o1 = offsets[e + 1], c = counts[e];
+      bad |= o0 < 0 || o1 < o0 || c < 0;
+    }
+  }
+  return __ballot(bad) != 0;
 }
 
 }  // namespace moe

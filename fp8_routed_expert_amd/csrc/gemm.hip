@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
     int E, int rows_total, int N, int K, uint16_t* __restrict__ C,
-    uint8_t* __restrict__ Q, void* __restrict__ QS) {
+    uint8_t* __restrict__ Q, void* __restrict__ QS, int32_t* __restrict__ status) {
   constexpr int NWM = BM / WM;
   constexpr int NWN = BN / WN;
   constexpr int NW = NWM * NWN;
@@ -302,6 +302,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
                              : total_mtiles<BM>(offsets, counts, E, rows_total, lane);
   const int total = total_m * n_tiles;
   const int logical = blockIdx.x;
+  // workgroup 0's first wave checks that offsets / counts describe segments
+  // (a corrupt table is still clipped to the buffer; rows past the tile
+  // count of the grid are then not computed, hence the flag)
+  if (!kDense && logical == 0 && threadIdx.x < 64 && status &&
+      segments_bad(offsets, counts, E, lane) && lane == 0)
+    atomicOr(status, MOE_ERR_BAD_INDEX);
   if (logical >= total) return;
   const int group_size = GM * n_tiles;
   const int grp = logical / group_size;
@@ -708,8 +714,8 @@ template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2 = false>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
-                           uint16_t* c, hipStream_t st, uint8_t* q = nullptr,
-                           void* q_scale = nullptr) {
+                           uint16_t* c, hipStream_t st, int32_t* status,
+                           uint8_t* q = nullptr, void* q_scale = nullptr) {
   if (N % BN != 0) return MOE_UNSUPPORTED_SHAPE;
   long long m_tiles = kTag == 3 ? ((long long)rows_total + BM - 1) / BM
                                 : (long long)rows_total / BM + E;
@@ -719,7 +725,7 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
   hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag, kPow2>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
-                     offsets, counts, E, rows_total, N, K, c, q, q_scale);
+                     offsets, counts, E, rows_total, N, K, c, q, q_scale, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
@@ -760,14 +766,25 @@ static bool use_big_tiles(long long rows_total, int N, int E) {
 
 using namespace moe;
 
+// The kernels address the row scales of the whole buffer through one buffer
+// descriptor, whose byte range and offsets are 32-bit: the scale array
+// (K/128 fp32 scales, or ceil(K/512) packed words, per row) must stay below
+// 0x7ffff000 bytes.  (The operand descriptors start at the tile's own rows
+// or weights and span far less.)
+static bool scale_span_ok(long long rows_total, int K, bool pow2) {
+  const long long kb = pow2 ? (K / kBK + 3) / 4 : K / kBK;
+  return kb * rows_total * 4 <= 0x7ffff000LL;
+}
+
 template <bool kPow2>
 static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w,
                                  const float* w_scale, const int32_t* offsets,
                                  const int32_t* counts, int E, int rows_total, int N, int K,
-                                 uint16_t* c, void* stream) {
+                                 uint16_t* c, int32_t* status, void* stream) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || N <= 0 || K <= 0)
     return MOE_INVALID_ARG;
   if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
+  if (!scale_span_ok(rows_total, K, kPow2)) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts || !w || !w_scale) return MOE_INVALID_ARG;
   if (rows_total == 0) return MOE_OK;
   if (!a || !a_scale || !c) return MOE_INVALID_ARG;
@@ -778,13 +795,13 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
   const bool big = use_big_tiles(rows_total, N, E);
   if (big)
     return gate_up ? launch<MOE_GEMM_BIG, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
-                                                    E, rows_total, N, K, c, st)
+                                                    E, rows_total, N, K, c, st, status)
                    : launch<MOE_GEMM_BIG, 2, kPow2>(a, a_scale, w, w_scale, offsets, counts,
-                                                    E, rows_total, N, K, c, st);
+                                                    E, rows_total, N, K, c, st, status);
   return gate_up ? launch<MOE_GEMM_SMALL, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
-                                                    E, rows_total, N, K, c, st)
+                                                    E, rows_total, N, K, c, st, status)
                  : launch<MOE_GEMM_SMALL, 2, kPow2>(a, a_scale, w, w_scale, offsets, counts,
-                                                    E, rows_total, N, K, c, st);
+                                                    E, rows_total, N, K, c, st, status);
 }
 
 extern "C" int moe_gemm_large_tiles(long long rows_total, int N, int E) {
@@ -797,30 +814,29 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(
     const float* w_scale, const int32_t* offsets, const int32_t* counts, int E,
     int rows_total, int N, int K, uint16_t* c, int32_t* status_dev,
     void* stream) {
-  (void)status_dev;
   return grouped_gemm<false>(a, a_scale, w, w_scale, offsets, counts, E, rows_total, N, K, c,
-                             stream);
+                             status_dev, stream);
 }
 
 extern "C" moe_status_t moe_grouped_gemm_fp8_e8m0(
     const uint8_t* a, const uint32_t* a_scale, const uint8_t* w, const uint32_t* w_scale,
     const int32_t* offsets, const int32_t* counts, int E, int rows_total, int N, int K,
     uint16_t* c, int32_t* status_dev, void* stream) {
-  (void)status_dev;
   return grouped_gemm<true>(a, reinterpret_cast<const float*>(a_scale), w,
                             reinterpret_cast<const float*>(w_scale), offsets, counts, E,
-                            rows_total, N, K, c, stream);
+                            rows_total, N, K, c, status_dev, stream);
 }
 
 template <bool kPow2>
 static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const uint8_t* w13,
                                 const float* w13_scale, const int32_t* offsets,
                                 const int32_t* counts, int E, int rows_total, int I, int H,
-                                uint8_t* q2, void* q2_scale, void* stream) {
+                                uint8_t* q2, void* q2_scale, int32_t* status, void* stream) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0 || H <= 0)
     return MOE_INVALID_ARG;
   if (I % kBlock != 0 || H % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
   if (2LL * I * H > 0x7ffff000LL) return MOE_UNSUPPORTED_SHAPE;   // one expert's W13 < 2 GB
+  if (!scale_span_ok(rows_total, H, kPow2)) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts || !w13 || !w13_scale) return MOE_INVALID_ARG;
   if (rows_total == 0) return MOE_OK;
   if (!a || !a_scale || !q2 || !q2_scale) return MOE_INVALID_ARG;
@@ -831,9 +847,10 @@ static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const ui
   const bool big = use_big_tiles(rows_total, N, E);
   if (big)
     return launch<MOE_GEMM_BIG, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
-                                          rows_total, N, H, nullptr, st, q2, q2_scale);
+                                          rows_total, N, H, nullptr, st, status, q2, q2_scale);
   return launch<MOE_GEMM_FUSED_SMALL, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
-                                                rows_total, N, H, nullptr, st, q2, q2_scale);
+                                                rows_total, N, H, nullptr, st, status, q2,
+                                                q2_scale);
 }
 
 extern "C" moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_scale,
@@ -842,9 +859,8 @@ extern "C" moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_sca
                                             int E, int rows_total, int I, int H, uint8_t* q2,
                                             float* q2_scale, int32_t* status_dev,
                                             void* stream) {
-  (void)status_dev;
   return gate_up_act<false>(a, a_scale, w13, w13_scale, offsets, counts, E, rows_total, I, H,
-                            q2, q2_scale, stream);
+                            q2, q2_scale, status_dev, stream);
 }
 
 extern "C" moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
@@ -853,10 +869,9 @@ extern "C" moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_
                                                  int E, int rows_total, int I, int H,
                                                  uint8_t* q2, uint32_t* q2_scale,
                                                  int32_t* status_dev, void* stream) {
-  (void)status_dev;
   return gate_up_act<true>(a, reinterpret_cast<const float*>(a_scale), w13,
                            reinterpret_cast<const float*>(w13_scale), offsets, counts, E,
-                           rows_total, I, H, q2, q2_scale, stream);
+                           rows_total, I, H, q2, q2_scale, status_dev, stream);
 }
 
 extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* w,
@@ -864,6 +879,7 @@ extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, con
                                      void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return MOE_INVALID_ARG;
   if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
+  if (!scale_span_ok(M, K, false)) return MOE_UNSUPPORTED_SHAPE;
   if (M == 0) return MOE_OK;
   if (!a || !a_scale || !w || !w_scale || !c) return MOE_INVALID_ARG;
   if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15) return MOE_UNSUPPORTED_SHAPE;
@@ -871,7 +887,7 @@ extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, con
   const bool big = use_big_tiles(M, N, 1);
   if (big)
     return launch<MOE_GEMM_BIG, 3>(a, a_scale, w, w_scale, nullptr, nullptr, 1, M, N, K, c,
-                                   st);
+                                   st, nullptr);
   return launch<MOE_GEMM_SMALL, 3>(a, a_scale, w, w_scale, nullptr, nullptr, 1, M, N, K, c,
-                                   st);
+                                   st, nullptr);
 }

@@ -157,8 +157,13 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, const uint8_t* x,
  *   offsets  [E+1], counts [E] int32 on the device (from moe_dispatch_layout)
  *   c        [rows_total, N] bf16; only valid rows are written
  * Segments reaching outside the buffer are clipped to it (rows the layout
- * call dropped are reported there, with MOE_ERR_OVERFLOW); status_dev is
- * accepted for uniformity and not written.
+ * call dropped are reported there, with MOE_ERR_OVERFLOW).  A table that
+ * does not describe segments (a negative start or count, or starts that
+ * decrease) sets MOE_ERR_BAD_INDEX in *status_dev (NULL: not reported); the
+ * rows computed are still clipped to the buffer, and some may be missing.
+ * MOE_UNSUPPORTED_SHAPE when the row-scale array (K/128 scales per row, or
+ * ceil(K/512) packed words) reaches 0x7ffff000 bytes: the kernels address it
+ * with 32-bit offsets.
  */
 moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
                                   const uint8_t* w, const float* w_scale,
@@ -183,7 +188,9 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t* a, const float* a_scale,
  *   w        [N, K] e4m3               w_scale [N/128, K/128] f32
  *   c        [M, N] bf16
  * N and K must be multiples of 128; M >= 0 is arbitrary (M = 0 launches
- * nothing).  No device status word: the call has no data-dependent errors.
+ * nothing); (K/128) * M * 4 bytes of row scales must stay below 0x7ffff000
+ * (MOE_UNSUPPORTED_SHAPE otherwise).  No device status word: the call has no
+ * data-dependent errors.
  */
 moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale,
                           const uint8_t* w, const float* w_scale, int M, int N,
@@ -201,8 +208,9 @@ moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale,
  *
  *   h        [rows_total, 2I] bf16
  *   q        [rows_total, I] e4m3     q_scale [I/128, rows_total] f32
- * I must be a multiple of 128 (MOE_UNSUPPORTED_SHAPE otherwise).
- * status_dev is accepted for uniformity and not written.
+ * I must be a multiple of 128 (MOE_UNSUPPORTED_SHAPE otherwise).  Valid
+ * rows come from offsets / counts as for moe_grouped_gemm_fp8, and a table
+ * that does not describe segments sets MOE_ERR_BAD_INDEX the same way.
  */
 moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
                              const int32_t* counts, int E, int rows_total,
@@ -226,9 +234,10 @@ moe_status_t moe_act_requant(const uint16_t* h, const int32_t* offsets,
  *   w13_scale [E, 2I/128, H/128] f32
  *   q2       [rows_total, I] e4m3      q2_scale [I/128, rows_total] f32
  * I and H must be multiples of 128 and one expert's W13 (2 I H bytes)
- * below 2 GB (MOE_UNSUPPORTED_SHAPE otherwise); a, w13 and q2 16-byte
- * aligned.  Rows outside every expert's valid range are not written.
- * status_dev is accepted for uniformity and not written.
+ * below 2 GB, and the row scales within moe_grouped_gemm_fp8's limit
+ * (MOE_UNSUPPORTED_SHAPE otherwise); a, w13 and q2 16-byte aligned.  Rows
+ * outside every expert's valid range are not written.  MOE_ERR_BAD_INDEX as
+ * for moe_grouped_gemm_fp8.
  */
 moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_scale,
                                  const uint8_t* w13, const float* w13_scale,
