@@ -102,11 +102,45 @@ def cpu_baseline(cfg, idx, w, n_tokens):
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = max(blas) if blas else 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": threads,
             "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} source tokens ({n_rows} routed rows), seeded; "
                       f"layout over all tokens; fp64 numpy, BLAS threads={threads}",
             "seconds": round(dt, 3), "rows_per_s": n_rows / dt,
             "stage_seconds": {k: round(v, 3) for k, v in stages.items()}}
+
+
+def measure_ceilings(dev, reps=5):
+    """What this GPU sustains, measured now with the library's helpers: a
+    plain 1 GiB device copy (2 GiB of HBM traffic) and a register-only chain
+    of the GEMMs' FP8 MFMA instruction.  Best of `reps` launches each."""
+    import torch
+    import fp8_routed_expert_amd as fre
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    sink = torch.zeros(2048, dtype=torch.float32, device=dev)
+
+    def best(fn):
+        fn()                                   # warm-up
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts), out
+    t_copy, _ = best(lambda: fre.moe_ceiling_copy(src, dst))
+    t_mfma, flops = best(lambda: fre.moe_ceiling_mfma_fp8(2048, 2000, sink))
+    del src, dst
+    return {"hbm_copy_gbs": round(2 * n / (t_copy * 1e-3) / 1e9, 1),
+            "fp8_mfma_tflops": round(flops / (t_mfma * 1e-3) / 1e12, 1),
+            "source": "measured in this run: moe_ceiling_copy (1 GiB device copy, read + "
+                      "write counted) and moe_ceiling_mfma_fp8 (register-only E4M3 "
+                      "16x16x128 MFMA chain), best of 5"}
 
 
 def bench_dense(args, M, N, K):
@@ -189,6 +223,11 @@ def main():
                          "(default: the layer's choice)")
     ap.add_argument("--fused", action="store_true",
                     help="run the gate/up GEMM with the activation fused (one call)")
+    ap.add_argument("--zipf", type=float, default=1.0,
+                    help="Zipf exponent of the per-expert load (the EP48 decode share, "
+                         "--config 3); 1.0 is the workload's, 0.613 gives hottest = 3x coldest")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the copy and MFMA ceilings")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first "
                          "(reference for scaling HBM byte counters)")
@@ -215,8 +254,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceil = None if args.no_ceilings else measure_ceilings(dev)
+    if ceil:
+        log(f"ceilings: copy {ceil['hbm_copy_gbs']} GB/s, FP8 MFMA {ceil['fp8_mfma_tflops']} TF/s")
     log(f"workload {cfg.name}: E={cfg.E} H={cfg.H} I={cfg.I} T={cfg.T} K={cfg.K}")
-    idx, w = routing(cfg)
+    if args.zipf != 1.0 and args.config != 3:
+        raise SystemExit("--zipf applies to --config 3 only")
+    idx, w = routing(cfg, zipf_s=args.zipf)
     R = int((idx >= 0).sum())
     xb = activations(cfg)
     w13b, w2b = weights(cfg)
@@ -300,8 +344,19 @@ def main():
     if st != 0:
         raise RuntimeError(f"device status word {st} after warm-up")
 
+    warm_ms = None
     scratch = None
     if args.flush_mib:
+        # the same steps without the flush first: the memory-side cache then
+        # holds what the previous step left (reported next to the flushed run)
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in wev:
+            e0.record()
+            run_step()
+            e1.record()
+        torch.cuda.synchronize()
+        warm_ms = [e0.elapsed_time(e1) for e0, e1 in wev]
         scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
@@ -358,11 +413,16 @@ def main():
                                f"{'masked' if cfg.layout else 'contiguous'} layout",
                    "experts": E, "hidden": H, "intermediate": I, "tokens": T,
                    "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total,
+                   **({"zipf_s": args.zipf} if args.config == 3 else {}),
                    "experts_with_rows": live, "block_scales": args.scales,
                    "gate_up_activation": "fused" if fused else "separate calls"},
         "timing": {"mode": "hipgraph replay" if graph is not None else "eager launches",
                    "cache_flush_mib": args.flush_mib,
-                   "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90)},
+                   "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90),
+                   **({"warm_step_ms_p10": round(float(np.percentile(warm_ms, 10)), 4),
+                       "warm_step_ms_p50": round(float(np.percentile(warm_ms, 50)), 4),
+                       "warm_step_ms_p90": round(float(np.percentile(warm_ms, 90)), 4)}
+                      if warm_ms is not None else {})},
         "mfma_peak_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
         "token_rows_per_s": round(R / (ms * 1e-3), 1),
     }
@@ -398,16 +458,35 @@ def main():
         # GEMM1 dominates every workload; below the ridge point (peak flop/s over
         # peak bytes/s) its bound is weight streaming from HBM
         ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        tsrc = ("stored: rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE of this kernel source and "
+                "launch, scaled by a 1 GiB copy (" + os.path.relpath(TRAFFIC_FILE, ROOT) + ")"
+                if traffic is not None else
+                "none: no counter record for this kernel source and launch")
         if flops1 / bytes_g1 >= ridge:
             result["roofline"] = {"kernel": kname, "bound": "mfma",
                                   "achieved": round(g1, 2), "peak": FP8_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(g1 / FP8_PEAK_TFLOPS, 4),
-                                  "traffic": traffic}
+                                  "traffic": traffic, "traffic_source": tsrc}
         else:
             result["roofline"] = {"kernel": kname, "bound": "hbm",
                                   "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                                  "traffic": traffic}
+                                  "traffic": traffic, "traffic_source": tsrc}
+        if ceil:
+            r = result["per_kernel_rate"]
+            fr = {"gemm1": round(r["gemm1_tflops"] / ceil["fp8_mfma_tflops"], 4)
+                  if flops1 / bytes_g1 >= ridge else
+                  round(r["gemm1_gbs"] / ceil["hbm_copy_gbs"], 4),
+                  "gemm2": round(r["gemm2_tflops"] / ceil["fp8_mfma_tflops"], 4)
+                  if flops2 / bytes_g2 >= ridge else
+                  round(r["gemm2_gbs"] / ceil["hbm_copy_gbs"], 4),
+                  "dispatch": round(r["dispatch_gbs"] / ceil["hbm_copy_gbs"], 4),
+                  "combine": round(r["combine_gbs"] / ceil["hbm_copy_gbs"], 4)}
+            if "act_gbs" in r:
+                fr["act"] = round(r["act_gbs"] / ceil["hbm_copy_gbs"], 4)
+            result["ceiling_frac"] = fr
+    if ceil:
+        result["ceilings"] = ceil
     if not args.no_cpu_baseline and args.scales == "fp32":
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(cfg, idx, w, args.cpu_tokens)

@@ -50,6 +50,8 @@ SIGNATURES = {
         _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_quantize_fp8": (ctypes.c_int32, [
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_ceiling_copy": (ctypes.c_int32, [_vp, _vp, _size, _vp]),
+    "moe_ceiling_mfma_fp8": (ctypes.c_int32, [_c_int, _c_int, _vp, _vp, _vp]),
 }
 
 ABI_VERSION = 5

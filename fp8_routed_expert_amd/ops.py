@@ -269,3 +269,24 @@ def moe_act_requant_e8m0(h, offsets, counts, q, q_scale, status, stream=None):
         _ptr(q_scale, _I32, "q_scale", (_words(I // 128), rows_total)),
         _ptr(status, _I32, "status", (1,)), _stream(stream))
     check(st, "moe_act_requant_e8m0")
+
+
+def moe_ceiling_copy(src, dst, stream=None):
+    """Copy src to dst (same byte size) with the library's plain copy kernel
+    (a measurement helper: HBM ceiling)."""
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst sizes differ")
+    n = src.numel() * src.element_size()
+    check(load().moe_ceiling_copy(_ptr(src, (src.dtype,), "src"), _ptr(dst, (dst.dtype,), "dst"),
+                                  n, _stream(stream)), "moe_ceiling_copy")
+
+
+def moe_ceiling_mfma_fp8(workgroups, iters, sink, stream=None):
+    """Launch the register-only FP8 MFMA chain; returns its flop count (a
+    measurement helper: matrix-core ceiling).  sink: float32 [workgroups]."""
+    import ctypes
+    fl = ctypes.c_double(0.0)
+    check(load().moe_ceiling_mfma_fp8(int(workgroups), int(iters),
+                                      _ptr(sink, _F32, "sink", (workgroups,)),
+                                      ctypes.byref(fl), _stream(stream)), "moe_ceiling_mfma_fp8")
+    return fl.value

@@ -336,6 +336,28 @@ moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
                                       uint8_t* q2, uint32_t* q2_scale,
                                       int32_t* status_dev, void* stream);
 
+/*
+ * Measurement helpers (not steps of the layer).  They time the two
+ * resources the layer's kernels are bound by, so that a kernel can be
+ * reported against what the GPU sustains as well as against its published
+ * peaks (HBM 8 TB/s, dense FP8 5.0 PFLOP/s).
+ *
+ * moe_ceiling_copy     dst[i] = src[i] for `bytes` bytes (a multiple of 16;
+ *                      both pointers 16-byte aligned, else INVALID_ARG): one
+ *                      16-byte load and store per lane, grid-stride.  Moves
+ *                      2 * bytes through HBM.
+ * moe_ceiling_mfma_fp8 `workgroups` workgroups of 4 waves, each wave running
+ *                      `iters` rounds of 8 independent E4M3 16x16x128 MFMAs
+ *                      on register operands (the instruction of the GEMMs);
+ *                      *flops (host pointer, may be NULL) receives the
+ *                      launch's flop count.  `sink` is a device array of
+ *                      `workgroups` floats that is (practically) never
+ *                      written; it keeps the chain from being optimised out.
+ */
+moe_status_t moe_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
+moe_status_t moe_ceiling_mfma_fp8(int workgroups, int iters, float* sink, double* flops,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif
