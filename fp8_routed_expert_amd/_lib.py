@@ -27,6 +27,9 @@ SIGNATURES = {
     "moe_dispatch_layout": (ctypes.c_int32, [
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
+    "moe_dispatch_layout_noalloc": (ctypes.c_int32, [
+        _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int32, [
         _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_quantize_fp8_e8m0": (ctypes.c_int32, [
@@ -54,7 +57,7 @@ SIGNATURES = {
     "moe_ceiling_mfma_fp8": (ctypes.c_int32, [_c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 

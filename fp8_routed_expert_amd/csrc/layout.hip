@@ -22,6 +22,8 @@
 //                  rows: one wave per piece of a source row, which reads
 //                  x[t] once and writes it to each of the token's slots
 //                  (16-byte accesses)
+#include <mutex>
+
 #include "device_common.hpp"
 
 namespace moe {
@@ -490,6 +492,54 @@ extern "C" moe_status_t moe_dispatch_layout(
                   H / kBlock, layout, align_m, rows, counts, offsets, slot_of, row_src,
                   row_expert, a, reinterpret_cast<uint32_t*>(a_scale), workspace,
                   workspace_bytes, status_dev, stream);
+}
+
+// ---------------------------------------------------------------------
+// Allocation-free dispatch.  The per-chunk histograms and bases live in a
+// file-scope device array instead of a caller workspace; each GPU holds its
+// own copy for the life of the process.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device with hipGetSymbolAddress and only that address is used.
+// The array needs no clearing: layout_count writes every histogram entry
+// the later kernels read, and layout_scan every base.
+constexpr size_t kScratchBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static moe_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_HIP_ERROR;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_HIP_ERROR;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_dispatch_layout_noalloc(
+    const int32_t* topk_idx, const uint8_t* x, const float* x_scale, int T, int K, int E,
+    int H, int layout, int align_m, int rows, int32_t* counts, int32_t* offsets,
+    int32_t* slot_of, int32_t* row_src, int32_t* row_expert, uint8_t* a, float* a_scale,
+    int32_t* status_dev, void* stream) {
+  if (T < 0 || K <= 0 || K > MOE_MAX_TOPK || E <= 0 || E > MOE_MAX_EXPERTS)
+    return MOE_INVALID_ARG;
+  if (moe_layout_workspace_bytes(T, K, E) > kScratchBytes) return MOE_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const moe_status_t r = scratch_on_current_device(&ws);
+  if (r != MOE_OK) return r;
+  return dispatch(topk_idx, x, reinterpret_cast<const uint32_t*>(x_scale), T, K, E, H,
+                  H / kBlock, layout, align_m, rows, counts, offsets, slot_of, row_src,
+                  row_expert, a, reinterpret_cast<uint32_t*>(a_scale), ws, kScratchBytes,
+                  status_dev, stream);
 }
 
 extern "C" moe_status_t moe_dispatch_layout_e8m0(

@@ -80,6 +80,30 @@ def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
     check(st, "moe_dispatch_layout")
 
 
+def moe_dispatch_layout_noalloc(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
+                                offsets, slot_of, row_src, row_expert, a, a_scale, status,
+                                stream=None):
+    """moe_dispatch_layout without a workspace: the library's fixed device
+    scratch holds the per-chunk histograms (nothing is allocated; calls that
+    overlap on one GPU race).  Raises on MOE_SCRATCH_LIMIT."""
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    rows_total = E * rows if layout == LAYOUT_MASKED else rows
+    lib = load()
+    st = lib.moe_dispatch_layout_noalloc(
+        _ptr(topk_idx, _I32, "topk_idx", (T, K)), _ptr(x, _U8, "x", (T, H)),
+        _ptr(x_scale, _F32, "x_scale", (T, H // 128)), T, K, E, H, layout,
+        align_m, rows, _ptr(counts, _I32, "counts", (E,)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)),
+        _ptr(slot_of, _I32, "slot_of", (T, K)),
+        _ptr(row_src, _I32, "row_src", (rows_total,)),
+        _ptr(row_expert, _I32, "row_expert", (rows_total,)),
+        _ptr(a, _U8, "a", (rows_total, H)),
+        _ptr(a_scale, _F32, "a_scale", (H // 128, rows_total)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, "moe_dispatch_layout_noalloc")
+
+
 def moe_grouped_gemm_fp8(a, a_scale, w, w_scale, offsets, counts, c, status,
                          stream=None):
     """c[valid rows] = block-scaled FP8 grouped GEMM of a with w[expert]."""

@@ -64,6 +64,7 @@ typedef int32_t moe_status_t;
 #define MOE_INVALID_ARG 1       /* null pointer, negative size, bad enum   */
 #define MOE_UNSUPPORTED_SHAPE 2 /* size not a multiple of 128, misaligned   */
 #define MOE_HIP_ERROR 3         /* a kernel launch failed                   */
+#define MOE_SCRATCH_LIMIT 4     /* beyond the allocation-free call's scratch */
 
 #define MOE_LAYOUT_CONTIGUOUS 0 /* prefill: expert segments stacked along M */
 #define MOE_LAYOUT_MASKED 1     /* decode: fixed [E, C, .] + device counts  */
@@ -136,6 +137,33 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, const uint8_t* x,
                                  float* a_scale, void* workspace,
                                  size_t workspace_bytes, int32_t* status_dev,
                                  void* stream);
+
+/*
+ * moe_dispatch_layout_noalloc — moe_dispatch_layout without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * hipGraph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, outputs, status bits and results as moe_dispatch_layout
+ * (bit for bit), minus workspace / workspace_bytes.
+ *
+ * The per-chunk histograms go to a fixed 1 MiB array in device memory
+ * owned by the library: each GPU the library runs on holds one such array
+ * until the process ends.  The call allocates nothing.  Limit:
+ * moe_layout_workspace_bytes(T, K, E) <= 1 MiB (about 4M routed entries at
+ * 32 experts); larger problems return MOE_SCRATCH_LIMIT and launch nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, or two host threads) race and give undefined results;
+ * serialise them.  The first call on each device resolves the array's
+ * device address (hipGetSymbolAddress, with that device current): make it
+ * outside stream capture; later calls are capturable.
+ */
+moe_status_t moe_dispatch_layout_noalloc(const int32_t* topk_idx, const uint8_t* x,
+                                         const float* x_scale, int T, int K, int E,
+                                         int H, int layout, int align_m, int rows,
+                                         int32_t* counts, int32_t* offsets,
+                                         int32_t* slot_of, int32_t* row_src,
+                                         int32_t* row_expert, uint8_t* a,
+                                         float* a_scale, int32_t* status_dev,
+                                         void* stream);
 
 /*
  * moe_grouped_gemm_fp8 — block-scaled FP8 grouped GEMM over the expert
