@@ -2,7 +2,8 @@
 parallelism.  The arithmetic lives in the HIP library libmoe_fp8.so (C ABI in
 include/moe_fp8.h); this package is its Python binding."""
 
-from .ops import (moe_layout_workspace_bytes, moe_gemm_large_tiles, moe_dispatch_layout,  # noqa: F401
+from .ops import (moe_layout_workspace_bytes, moe_gemm_large_tiles, moe_gemm_tile_rows,  # noqa: F401
+                  moe_dispatch_layout,
                   moe_dispatch_layout_noalloc,
                   moe_grouped_gemm_fp8, moe_gemm_fp8, moe_act_requant, moe_combine,
                   moe_quantize_fp8, moe_quantize_fp8_e8m0, moe_dispatch_layout_e8m0,

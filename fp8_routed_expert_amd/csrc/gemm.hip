@@ -75,6 +75,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup (gfx950)
 
 // Workgroup barrier for the tile pipeline.  __syncthreads() (and even an
 // LDS-scoped fence, since loads into LDS count as vector-memory operations)
@@ -115,6 +116,21 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint8_t* lds, uint32_t voff) {
   for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(voff), "s"(r) : "memory", "m0");
+}
+// The same with the offset split into a per-lane part and a wave-uniform
+// part added inside the asm: the compiler cannot then hoist one offset
+// register per chunk out of the K loop (the address is read when the load
+// issues, so the temporary is free right after).
+__device__ __forceinline__ void dma16_split(v4i rsrc, uint8_t* lds, uint32_t vlane,
+                                            uint32_t suni) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  uint32_t t;
+  asm volatile("v_add_u32_e32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\t"
+               "buffer_load_dwordx4 %0, %4, 0 offen lds"
+               : "=&v"(t) : "s"(suni), "v"(vlane), "s"(m), "s"(r) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -179,12 +195,26 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // gfx950, against 8 for the (r >> 1) & 7 and r & 7 permutations).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// 32 bytes of row `row` of a swizzled tile: logical 16-byte chunks 2g, 2g+1.
-__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int g) {
-  const uint8_t* base = tile + row * kBK;
-  const int sw = swz(row);
-  uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * g) ^ sw) << 4));
-  uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * g + 1) ^ sw) << 4));
+// A lane's byte offsets, within a stage, of the two 16-byte chunks (logical
+// 2g and 2g + 1) it reads from row row0 + r16 of a swizzled tile.  For any
+// row0 that is a multiple of 16 the permutation of row row0 + 16 i + r16
+// is that of r16, so the fragment of subtile row i lies a fixed 16 i * 128
+// bytes further: one pair of offsets serves every subtile of a wave.
+struct FragLane {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ FragLane frag_lane(int row0, int r16, int g) {
+  const uint32_t r = (uint32_t)(row0 + r16) * kBK;
+  const int sw = swz(r16);
+  return {r + (uint32_t)(((2 * g) ^ sw) << 4), r + (uint32_t)(((2 * g + 1) ^ sw) << 4)};
+}
+
+// 32 bytes of a fragment: the lane's two chunks, `off` bytes (a multiple of
+// 16 rows) past its offsets in stage `tile`.
+__device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, int off, FragLane fl) {
+  const uint8_t* base = tile + off;
+  uint4 lo = *reinterpret_cast<const uint4*>(base + fl.lo);
+  uint4 hi = *reinterpret_cast<const uint4*>(base + fl.hi);
   v8i r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
@@ -237,6 +267,20 @@ __device__ __forceinline__ int total_mtiles(const int32_t* offsets, const int32_
   return __builtin_amdgcn_readfirstlane(total);
 }
 
+// The third A stage, an LDS object only where the kernel has one (a tile
+// whose two A and two B stages already fill the LDS declares none).
+template <int kBytes>
+struct ThirdStage {
+  __device__ __forceinline__ static uint8_t* get() {
+    __shared__ __attribute__((aligned(1024))) uint8_t s[kBytes];
+    return s;
+  }
+};
+template <>
+struct ThirdStage<0> {
+  __device__ __forceinline__ static uint8_t* get() { return nullptr; }
+};
+
 // Expert, first row and segment end of m-tile mt (e_sel = -1 if none).
 template <int BM>
 __device__ __forceinline__ void find_mtile(const int32_t* offsets, const int32_t* counts,
@@ -279,7 +323,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   constexpr int CA = A_CHUNKS / NW;                  // A / B chunks per wave and stage
   constexpr int CB = B_CHUNKS / NW;
   static_assert(A_CHUNKS % NW == 0 && B_CHUNKS % NW == 0, "chunks must split evenly");
-  static_assert(CA % 2 == 0 && CB % 2 == 0, "chunk parity is static");
+  static_assert(CB % 2 == 0, "B chunk parity is static");
   static_assert(BN <= kBlock || BN % kBlock == 0, "tile N range");
   static_assert(WN <= kBlock && kBlock % WN == 0, "wave columns in one scale block");
   static_assert(CA < 64, "vmcnt range");
@@ -293,15 +337,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   static_assert(!kFused || (WN == 64 && NJ == 4 && BN / 2 == kBlock), "fused tile shape");
 
   // A rows: three stages (k-blocks kb, kb + 1 landed or landing, kb + 2
-  // in flight); B rows: two stages.  Each stage is its own LDS object.
+  // in flight) when they fit beside the two B stages, else two (320-row
+  // tiles: kb + 1 is loaded while kb is multiplied, like B).  Each stage is
+  // its own LDS object.
   constexpr int SA_B = BM * kBK, SB_B = BN * kBK;
+  constexpr int NSA = 3 * SA_B + 2 * SB_B <= kLdsBytes ? 3 : 2;
+  static_assert(NSA * SA_B + 2 * SB_B <= kLdsBytes, "tile stages exceed the LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA_B];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA_B];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA2[SA_B];
+  uint8_t* const sA2 = ThirdStage<NSA == 3 ? SA_B : 0>::get();   // null with two stages
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB_B];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB_B];
-  uint8_t* const stA[3] = {sA0, sA1, sA2};
-  uint8_t* const stB[2] = {sB0, sB1};
+  // stage by (compile-time) index
+  auto stA = [&](int i) -> uint8_t* { return i == 0 ? sA0 : i == 1 ? sA1 : sA2; };
+  auto stB = [&](int i) -> uint8_t* { return i == 0 ? sB0 : sB1; };
 
   // ---- which tile: grouped order over the tile list (see the XCD note above)
   constexpr bool kDense = kTag == 3;
@@ -376,8 +425,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int wcol = wn * WN;
-  static_assert(MI % 4 == 0, "row scales are loaded 64 rows at a time");
-  constexpr int NR = MI / 4;
+  // fragment read offsets of the wave's A rows and B columns
+  FragLane fa = frag_lane(wm * WM, r16, g);
+  FragLane fb = frag_lane(wcol, r16, g);
+  constexpr int NR = (MI + 3) / 4;   // 64-row scale loads (the last may overhang)
   const uint32_t srow = (uint32_t)(row0 + wm * WM + lane);
   float fs_raw[NR];
 #pragma unroll
@@ -386,22 +437,30 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // filled when its load completes, not when the instruction issues, so
   // fs_raw is read only after the wait_loads() that covers these loads,
   // which is also where the compiler sees the values being written.
-  auto load_scales = [&](int kb) {
-    const uint32_t base = ((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total + srow) * 4u;
+  // Loads that a step issues past the last k-block (live = false) take an
+  // offset beyond every descriptor's range: they read zero without touching
+  // memory, and every step issues the same loads and ends with the same
+  // wait, with no branch in the step (a branch per wait left the compiler's
+  // control flow with paths no execution takes).
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  auto load_scales = [&](int kb, bool live) {
+    const uint32_t base =
+        live ? ((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total + srow) * 4u : kOutOfRange;
 #pragma unroll
     for (int c = 0; c < NR; ++c)
       asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3"
                    : "=v"(fs_raw[c]) : "v"(base), "s"(rsrc_s), "n"(c * 256) : "memory");
   };
-  auto issue_a1 = [&](int kb, uint8_t* tA, int u) {
-    const int c = wave * CA + u;   // wave-uniform; parity of c is u's
-    dma16(rsrc_a, tA + c * 1024,
-          ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)(c * 8) * (uint32_t)K +
-              (uint32_t)kb * kBK);
+  auto issue_a1 = [&](int kb, uint8_t* tA, int u, bool live) {
+    const int c = wave * CA + u;   // wave-uniform; with CA even its parity is u's
+    const bool odd = CA % 2 == 0 ? (u & 1) : (c & 1);
+    dma16_split(rsrc_a, tA + c * 1024, odd ? lane_off1 : lane_off0,
+                __builtin_amdgcn_readfirstlane(
+                    live ? (uint32_t)(c * 8) * (uint32_t)K + (uint32_t)kb * kBK : kOutOfRange));
   };
-  auto issue_a = [&](int kb, uint8_t* tA) {
+  auto issue_a = [&](int kb, uint8_t* tA, bool live) {
 #pragma unroll
-    for (int u = 0; u < CA; ++u) issue_a1(kb, tA, u);
+    for (int u = 0; u < CA; ++u) issue_a1(kb, tA, u, live);
   };
   // kLateA: the A rows of k-block kb + 2 are issued after the MFMAs of the
   // first subtile row of step kb instead of with the B rows at its start.
@@ -413,10 +472,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // all the tile loads, was slower); the fused kernel keeps the early
   // issue, with which it needs no register spills.
   constexpr bool kLateA = !kFused;
-  auto issue_a_row = [&](int kb, uint8_t* tA, int i) {
-    if (i == 1) issue_a(kb, tA);   // MI >= 4
+  auto issue_a_row = [&](int kb, uint8_t* tA, int i, bool live) {
+    if (i == 1) issue_a(kb, tA, live);   // MI >= 4
   };
-  auto issue_b = [&](int kb, uint8_t* tB) {
+  auto issue_b = [&](int kb, uint8_t* tB, bool live) {
     const uint32_t kofs = (uint32_t)kb * kBK;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
@@ -426,8 +485,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
         const int wv = row / WN, k = row - wv * WN;
         row = (k < WN / 2 ? 0 : Ih - WN / 2) + ni0 + wv * (WN / 2) + k;
       }
-      dma16(rsrc_b, tB + c * 1024,
-            ((u & 1) ? lane_off1 : lane_off0) + (uint32_t)row * (uint32_t)K + kofs);
+      dma16_split(rsrc_b, tB + c * 1024, (u & 1) ? lane_off1 : lane_off0,
+                  __builtin_amdgcn_readfirstlane(live ? (uint32_t)row * (uint32_t)K + kofs
+                                                      : kOutOfRange));
     }
   };
 
@@ -451,11 +511,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   v8i bf[NJ];
   v8i af_next;
 
-  // One K step: A k-block kb in A stage SAi = kb % 3, B in B stage
+  // One K step: A k-block kb in A stage SAi = kb % NSA, B in B stage
   // SBi = kb % 2.  At its start the B rows and row scales of k-block kb + 1
-  // and the A rows of k-block kb + 2 are issued (into stages freed by the
-  // barrier that ended the previous step's reads).  At the step barrier
-  // only the A rows of kb + 2 may still be in flight.
+  // and the A rows of k-block kb + NSA - 1 are issued (into stages freed by
+  // the barrier that ended the previous step's reads).  At the step barrier
+  // only the A rows of kb + 2 may still be in flight (three A stages; with
+  // two, every load of kb + 1 has landed).
   //
   // Packed scales: the step barrier comes once the wave's last LDS read of
   // the step (the A fragment of the last subtile row) has landed, before
@@ -464,34 +525,39 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // idle while they load.  Measured at the prefill gate/up shape: 7% off the
   // GEMM, 5% off the fused GEMM + activation, 4% off the down GEMM, with
   // bit-identical results.
-  auto step = [&](int kb, auto sa_i, auto sb_i) {
+  auto step = [&](int kb, auto sa_i, auto sb_i) __attribute__((always_inline)) {
     constexpr int SAi = decltype(sa_i)::value;
     constexpr int SBi = decltype(sb_i)::value;
-    const uint8_t* tA = stA[SAi];
-    const uint8_t* tAn = stA[(SAi + 1) % 3];   // next step's stages
-    const uint8_t* tBn = stB[(SBi + 1) % 2];
-    float fs[MI];
+    // opaque per step: the compiler then forms each fragment address inside
+    // the step (lane offset + immediate) instead of hoisting one register
+    // per stage and subtile out of the K loop
+    asm volatile("" : "+v"(fa.lo), "+v"(fa.hi), "+v"(fb.lo), "+v"(fb.hi));
+    const uint8_t* tA = stA(SAi);
+    const uint8_t* tAn = stA((SAi + 1) % NSA);   // next step's stages
+    const uint8_t* tBn = stB((SBi + 1) % 2);
+    float fs[4 * NR];
 #pragma unroll
     for (int c = 0; c < NR; ++c) row_scales(fs_raw[c], fs + 4 * c);
     const bool rb = kb + 1 < Kb;
-    const bool ra = kb + 2 < Kb;
-    if (rb) {
-      issue_b(kb + 1, stB[(SBi + 1) % 2]);
-      load_scales(kb + 1);
-    }
-    if (ra && !kLateA) issue_a(kb + 2, stA[(SAi + 2) % 3]);
+    const bool ra = kb + NSA - 1 < Kb;   // A rows of k-block kb + NSA - 1 to load
+    uint8_t* const tAl = stA((SAi + NSA - 1) % NSA);
+    issue_b(kb + 1, stB((SBi + 1) % 2), rb);
+    load_scales(kb + 1, rb);
+    if (!kLateA) issue_a(kb + NSA - 1, tAl, ra);
     const float sw = sw_cur;
     const float swu = swu_cur;
+    const int kn = rb ? kb + 1 : kb;   // the next step's k-block (the last: unused)
     if (kFused) {
-      sw_cur = rb ? SWg[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
-      swu_cur = rb ? SWu[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+      sw_cur = SWg[kPow2 ? kn >> 2 : kn];
+      swu_cur = SWu[kPow2 ? kn >> 2 : kn];
     } else {
-      sw_cur = rb ? SWw[kPow2 ? (kb + 1) >> 2 : kb + 1] : 0.f;
+      sw_cur = SWw[kPow2 ? kn >> 2 : kn];
     }
     // the end of the step's reads: wait for the loads of k-block kb + 1
-    // (everything but the A rows of kb + 2), then meet the other waves
+    // (with three A stages everything but the A rows of kb + 2), then meet
+    // the other waves
     auto end_reads = [&]() {
-      if (ra)
+      if constexpr (NSA == 3)
         wait_loads<CA>(fs_raw);
       else
         wait_loads<0>(fs_raw);
@@ -506,9 +572,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
       for (int i = 0; i < MI; ++i) sa_e[i] = (int)((__float_as_uint(fs[i]) >> sh) & 0xffu);
 #pragma unroll
       for (int i = 0; i < MI - 1; ++i) {
-        if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
+        if (kLateA) issue_a_row(kb + NSA - 1, tAl, i, ra);
         const v8i af = af_next;
-        af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
+        af_next = load_frag_at(tA, (i + 1) * 16 * kBK, fa);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -529,9 +595,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
         acc[MI - 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             bf[j], af, acc[MI - 1][j], 0, 0, 0, (kFused && j >= NJ / 2) ? swu_e : sw_e, 0,
             sa_e[MI - 1]);
-        bf[j] = load_frag(tBn, wcol + j * 16 + r16, g);
+        bf[j] = load_frag_at(tBn, j * 16 * kBK, fb);
       }
-      af_next = load_frag(tAn, wm * WM + r16, g);
+      af_next = load_frag_at(tAn, 0, fa);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -550,13 +616,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     // fprev persist across steps), so a wave reaches the step barrier right
     // after issuing its last MFMA instead of waiting for it to finish.
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bf[j] = load_frag(stB[SBi], wcol + j * 16 + r16, g);
-    af_next = load_frag(tA, wm * WM + r16, g);
+    for (int j = 0; j < NJ; ++j) bf[j] = load_frag_at(stB(SBi), j * 16 * kBK, fb);
+    af_next = load_frag_at(tA, 0, fa);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      if (kLateA && ra) issue_a_row(kb + 2, stA[(SAi + 2) % 3], i);
+      if (kLateA) issue_a_row(kb + NSA - 1, tAl, i, ra);
       const v8i af = af_next;
-      if (i + 1 < MI) af_next = load_frag(tA, wm * WM + (i + 1) * 16 + r16, g);
+      if (i + 1 < MI) af_next = load_frag_at(tA, (i + 1) * 16 * kBK, fa);
       const float fcur = fs[i] * sw;
       const float fcuru = kFused ? fs[i] * swu : 0.f;
       v4f tcur[NJ];
@@ -599,11 +665,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   } else {
     sw_cur = SWw[0];
   }
-  issue_b(0, sB0);
-  load_scales(0);
-  issue_a(0, sA0);
-  if (Kb > 1) {
-    issue_a(1, sA1);
+  issue_b(0, sB0, true);
+  load_scales(0, true);
+  issue_a(0, sA0, true);
+  if constexpr (NSA == 3) {
+    issue_a(1, sA1, Kb > 1);
     wait_loads<CA>(fs_raw);
   } else {
     wait_loads<0>(fs_raw);
@@ -611,19 +677,29 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   lds_barrier();
   if constexpr (kPow2) {   // fp32 scales: read at the step start
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bf[j] = load_frag(sB0, wcol + j * 16 + r16, g);
-    af_next = load_frag(sA0, wm * WM + r16, g);
+    for (int j = 0; j < NJ; ++j) bf[j] = load_frag_at(sB0, j * 16 * kBK, fb);
+    af_next = load_frag_at(sA0, 0, fa);
   }
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
+  // unrolled by 6 = lcm(3, 2), so every step names its stages statically
+  auto step_u = [&](int kb, auto u) __attribute__((always_inline)) {
+    constexpr int U = decltype(u)::value;
+    if (U == 0 || kb < Kb)
+      step(kb, std::integral_constant<int, U % NSA>(), std::integral_constant<int, U % 2>());
+  };
   for (int kb = 0; kb < Kb; kb += 6) {
-    step(kb, I0(), I0());
-    if (kb + 1 < Kb) step(kb + 1, I1(), I1());
-    if (kb + 2 < Kb) step(kb + 2, I2(), I0());
-    if (kb + 3 < Kb) step(kb + 3, I0(), I1());
-    if (kb + 4 < Kb) step(kb + 4, I1(), I0());
-    if (kb + 5 < Kb) step(kb + 5, I2(), I1());
+    step_u(kb, std::integral_constant<int, 0>());
+    step_u(kb + 1, std::integral_constant<int, 1>());
+    step_u(kb + 2, std::integral_constant<int, 2>());
+    step_u(kb + 3, std::integral_constant<int, 3>());
+    step_u(kb + 4, std::integral_constant<int, 4>());
+    step_u(kb + 5, std::integral_constant<int, 5>());
+  }
+  // With three A stages the last step leaves its (out-of-range, zero)
+  // A loads in flight; they write into stage memory, which the epilogue
+  // reuses, so every wave drains its loads and meets the others first.
+  if constexpr (NSA == 3) {
+    wait_loads<0>(fs_raw);
+    lds_barrier();
   }
   if constexpr (!kPow2) {   // the last row's products
 #pragma unroll
@@ -646,8 +722,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     // activation kernel computes it, the row's 1x128 amax over the NWN waves
     // through LDS, E4M3 codes staged in LDS (16-byte chunks XOR-permuted by
     // row & 7) and stored as 128-byte row pieces, one scale per row.  The
-    // stage memory is free: the last step waited for every load and ended
-    // with a barrier.
+    // stage memory is free: every load has landed and all waves have met
+    // since the last fragment read.
     (void)C;
     constexpr int NT = 64 * NW;
     static_assert(BM * NWN * 4 <= SA_B && BM * kBlock <= SA_B, "fused staging space");
@@ -720,8 +796,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     // 4g .. 4g+3.  Stored directly, every store instruction would write 16
     // scattered 32-byte pieces; instead each wave stages its WM x WN bf16
     // sub-tile (rows of WN * 2 = 128 bytes) in a region of its own in the
-    // stage memory -- free now: the last step waited for every load and ended
-    // with a barrier -- and stores it back as 16-byte pieces, eight lanes per
+    // stage memory -- free now: every load has landed and all waves have met
+    // since the last fragment read -- and stores it back as 16-byte pieces, eight lanes per
     // contiguous 128-byte row.  Only the wave's own LDS accesses are ordered,
     // so no workgroup barrier is needed.  The 8-byte chunks of staged row r
     // are XOR-permuted by 2 * ((r >> 1) & 7), which keeps the chunk pairs of
@@ -730,48 +806,55 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
     // direct 8-byte stores; the packed hardware conversion to bf16 took
     // another 6% (GEMM2) and 3% (GEMM1) off against a bit-level rounding
     // sequence.
-    constexpr int kRegion = WM * WN * 2;
-    constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
+    // A wave's sub-tile is staged in kParts passes of PM rows when the free
+    // stage memory cannot hold all NW of them at once (320-row tiles: two).
     static_assert(WN * 2 == 128, "staged rows are 128 bytes");
-    static_assert(kPerA >= 1 && kPerB >= 1 && NW <= 3 * kPerA + 2 * kPerB, "staging space");
-    uint8_t* region;
-    {
-      int w = wave;
-      if (w < kPerA) {
-        region = sA0 + w * kRegion;
-      } else if ((w -= kPerA) < kPerA) {
-        region = sA1 + w * kRegion;
-      } else if ((w -= kPerA) < kPerA) {
-        region = sA2 + w * kRegion;
-      } else if ((w -= kPerA) < kPerB) {
-        region = sB0 + w * kRegion;
-      } else {
-        region = sB1 + (w - kPerB) * kRegion;
-      }
+    constexpr auto fits = [](int parts) {
+      const int region = WM / parts * WN * 2;
+      return (SA_B / region) * NSA + (SB_B / region) * 2 >= NW;
+    };
+    constexpr int kParts = fits(1) ? 1 : fits(2) ? 2 : (MI % 3 == 0 && fits(3)) ? 3
+                         : (MI % 4 == 0 && fits(4)) ? 4 : 5;
+    static_assert(fits(kParts) && MI % kParts == 0, "staging space");
+    constexpr int PM = WM / kParts;            // rows per pass
+    constexpr int kRegion = PM * WN * 2;
+    constexpr int kPerA = SA_B / kRegion, kPerB = SB_B / kRegion;
+    uint8_t* region;   // regions fill the A stages, then the B stages
+    if (wave < NSA * kPerA) {
+      const int st = wave / kPerA;
+      region = (st == 0 ? sA0 : st == 1 ? sA1 : sA2) + (wave - st * kPerA) * kRegion;
+    } else {
+      const int w = wave - NSA * kPerA;
+      region = w < kPerB ? sB0 + w * kRegion : sB1 + (w - kPerB) * kRegion;
     }
-  #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = i * 16 + r16;
-      const int f = ((r >> 1) & 7) << 1;
-  #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        uint2 o;
-        o.x = pack2_bf16(acc[i][j][0], acc[i][j][1]);
-        o.y = pack2_bf16(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<uint2*>(region + r * 128 + (((j * 4 + g) ^ f) << 3)) = o;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int c16 = lane & 7;
   #pragma unroll
-    for (int rr = 0; rr < WM; rr += 8) {
-      const int r = rr + (lane >> 3);
-      const uint4 v =
-          *reinterpret_cast<const uint4*>(region + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
-      const int row = row0 + wm * WM + r;
-      if (row < row_end)   // streamed out: not kept in the caches the tiles share
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
-                                    reinterpret_cast<u32x4*>(C + (size_t)row * N + n0 + wcol + c16 * 8));
+    for (int part = 0; part < kParts; ++part) {
+      // the stores of a pass consume the values it read back, so those
+      // reads have completed before the next pass overwrites the region
+  #pragma unroll
+      for (int i = part * (MI / kParts); i < (part + 1) * (MI / kParts); ++i) {
+        const int r = (i - part * (MI / kParts)) * 16 + r16;
+        const int f = ((r >> 1) & 7) << 1;
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          uint2 o;
+          o.x = pack2_bf16(acc[i][j][0], acc[i][j][1]);
+          o.y = pack2_bf16(acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<uint2*>(region + r * 128 + (((j * 4 + g) ^ f) << 3)) = o;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  #pragma unroll
+      for (int rr = 0; rr < PM; rr += 8) {
+        const int r = rr + (lane >> 3);
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(region + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
+        const int row = row0 + wm * WM + part * PM + r;
+        if (row < row_end)   // streamed out: not kept in the caches the tiles share
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                      reinterpret_cast<u32x4*>(C + (size_t)row * N + n0 + wcol + c16 * 8));
+      }
     }
   }
 }
@@ -807,6 +890,14 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 #ifndef MOE_GEMM_SMALL
 #define MOE_GEMM_SMALL 128, 128, 64, 64, 4
 #endif
+// Packed scales at prefill sizes: 320 x 256 tiles of 8 waves of 160 x 64
+// (160 accumulator registers per lane; two A and two B stages, 144 KB of
+// LDS), which the scaled MFMA's in-place accumulation leaves room for.
+// 384-row tiles (192 accumulators) do not fit two waves per SIMD without
+// spilling.
+#ifndef MOE_GEMM_HUGE
+#define MOE_GEMM_HUGE 320, 256, 160, 64, 2
+#endif
 // The fused gate/up + activation kernel needs a tile to cover one whole
 // 1x128 block of intermediate columns (BN = 256: 128 gate + 128 up
 // columns): large problems use MOE_GEMM_BIG, small ones 128 x 256 tiles of
@@ -826,6 +917,16 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 // slower for the masked layout had it used large tiles.
 static bool use_big_tiles(long long rows_total, int N, int E) {
   return N % 256 == 0 && rows_total >= 256LL * E && (rows_total / 256) * (N / 256) > 128;
+}
+
+// 320-row tiles (packed scales only): a tile then receives 72 KB per k-step
+// for 320 x 256 outputs instead of 64 KB for 256 x 256, 10% fewer bytes per
+// flop through the per-CU feed that bounds the large tiles.  Taken when the
+// segments average at least 4096 rows (the partial last tile of each
+// expert then wastes a few percent at most) and the tiles fill every CU.
+static bool use_huge_tiles(long long rows_total, int N, int E) {
+  return use_big_tiles(rows_total, N, E) && rows_total >= 4096LL * E &&
+         (rows_total / 320) * (N / 256) >= 256;
 }
 
 }  // namespace moe
@@ -859,6 +960,11 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
   const bool gate_up = K > N;   // gate/up: K = H > N = 2I; down: N = H > K = I
   // host-known sizes only, so the choice is the same inside graph capture
   const bool big = use_big_tiles(rows_total, N, E);
+  if (kPow2 && use_huge_tiles(rows_total, N, E))
+    return gate_up ? launch<MOE_GEMM_HUGE, 1, true>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st, status)
+                   : launch<MOE_GEMM_HUGE, 2, true>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st, status);
   if (big)
     return gate_up ? launch<MOE_GEMM_BIG, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
                                                     E, rows_total, N, K, c, st, status)
@@ -873,6 +979,14 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
 extern "C" int moe_gemm_large_tiles(long long rows_total, int N, int E) {
   if (rows_total <= 0 || N <= 0 || E <= 0) return -1;
   return use_big_tiles(rows_total, N, E) ? 1 : 0;
+}
+
+static constexpr int tile_rows(int bm, int, int, int, int) { return bm; }
+
+extern "C" int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales) {
+  if (rows_total <= 0 || N <= 0 || E <= 0) return -1;
+  if (packed_scales && use_huge_tiles(rows_total, N, E)) return tile_rows(MOE_GEMM_HUGE);
+  return use_big_tiles(rows_total, N, E) ? tile_rows(MOE_GEMM_BIG) : tile_rows(MOE_GEMM_SMALL);
 }
 
 extern "C" moe_status_t moe_grouped_gemm_fp8(
@@ -911,6 +1025,9 @@ static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const ui
   const int N = 2 * I;
   // the same host-side rule as the unfused gate/up GEMM
   const bool big = use_big_tiles(rows_total, N, E);
+  if (kPow2 && use_huge_tiles(rows_total, N, E))
+    return launch<MOE_GEMM_HUGE, 4, true>(a, a_scale, w13, w13_scale, offsets, counts, E,
+                                          rows_total, N, H, nullptr, st, status, q2, q2_scale);
   if (big)
     return launch<MOE_GEMM_BIG, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
                                           rows_total, N, H, nullptr, st, status, q2, q2_scale);

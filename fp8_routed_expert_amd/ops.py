@@ -49,9 +49,16 @@ def moe_layout_workspace_bytes(T, K, E):
 
 
 def moe_gemm_large_tiles(rows_total, N, E):
-    """1 if the GEMM calls run this size with 256 x 256 tiles, 0 if with the
+    """1 if the GEMM calls run this size with large tiles, 0 if with the
     small tiles, -1 for non-positive sizes (the library's host-side rule)."""
     return int(load().moe_gemm_large_tiles(int(rows_total), int(N), int(E)))
+
+
+def moe_gemm_tile_rows(rows_total, N, E, packed_scales=False):
+    """Row height (320, 256 or 128) of the output tiles the GEMM calls use
+    for this size; packed_scales for the *_e8m0 calls.  -1 for
+    non-positive sizes."""
+    return int(load().moe_gemm_tile_rows(int(rows_total), int(N), int(E), int(bool(packed_scales))))
 
 
 def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,

@@ -89,13 +89,20 @@ size_t moe_layout_workspace_bytes(int T, int K, int E);
 
 /* Whether the grouped GEMM calls (moe_grouped_gemm_fp8, moe_gate_up_act_fp8,
  * their _e8m0 forms; N = 2I for the gate/up projection) and moe_gemm_fp8
- * (E = 1, rows_total = M) run a problem of this size with 256 x 256 tiles
- * (1) or 128 x 128 (0; 128 x 256 for the fused gate/up + activation).  A
- * host-side rule of the sizes alone, so it is the same under graph capture;
- * the rule itself is stated where it is implemented.  Returns -1 for
- * negative or zero sizes.  Callers use it to choose between the fused and
- * the separate gate/up + activation calls. */
+ * (E = 1, rows_total = M) run a problem of this size with large tiles (1:
+ * 256 x 256, or 320 x 256 for the _e8m0 calls at the sizes where
+ * moe_gemm_tile_rows says so) or small ones (0: 128 x 128; 128 x 256 for
+ * the fused gate/up + activation).  A host-side rule of the sizes alone, so
+ * it is the same under graph capture; the rule itself is stated where it is
+ * implemented.  Returns -1 for negative or zero sizes.  Callers use it to
+ * choose between the fused and the separate gate/up + activation calls. */
 int moe_gemm_large_tiles(long long rows_total, int N, int E);
+
+/* The row height of the output tiles those calls use for this size: 320,
+ * 256 or 128.  packed_scales != 0 asks about the _e8m0 calls (the only ones
+ * with 320-row tiles), 0 about the fp32-scale calls.  -1 for negative or
+ * zero sizes. */
+int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales);
 
 /*
  * moe_dispatch_layout — count, prefix-sum, stably rank and permute the

@@ -146,3 +146,11 @@ def test_gemm_tile_rule():
     assert f(8192, 4096, 1) == 1        # dense, 32 x 16 large tiles
     assert f(2048, 4096, 1) == 0        # dense, 8 x 16 = 128: not more than half the CUs
     assert f(0, 4096, 1) == -1 and f(256, 0, 1) == -1 and f(256, 256, 0) == -1
+    rows = lib.moe_gemm_tile_rows
+    assert rows(132183, 4096, 9, 1) == 320   # prefill share, packed scales
+    assert rows(132183, 7168, 9, 1) == 320
+    assert rows(132183, 4096, 9, 0) == 256   # fp32 scales keep 256 x 256
+    assert rows(6906, 4096, 6, 1) == 256     # decode: segments under 4096 rows
+    assert rows(13135, 2048, 3, 1) == 320    # the synthetic 320-row test shape
+    assert rows(4096, 4096, 32, 1) == 128
+    assert rows(0, 4096, 1, 1) == -1

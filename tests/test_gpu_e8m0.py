@@ -94,6 +94,60 @@ def test_gemm_e8m0_exact_integers(gpu):
             assert np.array_equal(bf16_decode(got[s:en]), ref), e
 
 
+@pytest.mark.parametrize("K", [128, 384, 640])
+def test_gemm_e8m0_exact_integers_320_row_tiles(gpu, K):
+    """The 320 x 256 tiles of the packed path (two A stages) on exact
+    small-integer data: one, three and five k-blocks, a 5-row expert, an
+    empty one and a long ragged one whose tiles straddle its end.  Sampled
+    rows (segment ends, every tile boundary, random rows) equal the oracle
+    bit for bit; rows outside the segments are never written; and the fused
+    gate/up + activation call on the same tiles equals the GEMM followed by
+    the activation call bit for bit."""
+    g = np.random.default_rng(37 + K)
+    E, N = 3, 2048
+    counts = np.array([5, 0, 13123])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    R = int(offsets[-1]) + 7
+    assert fre.moe_gemm_tile_rows(R, N, E, True) == 320
+    a = e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float64))
+    w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
+    ea = g.integers(-2, 3, (R, K // 128)).astype(np.int32)
+    ew = g.integers(-2, 3, (E, N // 128, K // 128)).astype(np.int32)
+    log(f"320-row tiles: R={R} N={N} K={K} E={E}")
+    got = _run_gemm_e8m0(a, ea, w, ew, offsets, counts)
+    inside = np.zeros(R, bool)
+    for e in range(E):
+        s, en = int(offsets[e]), int(offsets[e] + counts[e])
+        if en <= s:
+            continue
+        inside[s:en] = True
+        rows = {s, en - 1}
+        rows |= {r for t in range(1, (en - s) // 320 + 1) for r in (s + 320 * t - 1, s + 320 * t)
+                 if r < en}
+        rows |= set(g.integers(s, en, 24).tolist())
+        rows = np.array(sorted(rows))
+        ref = moe.gemm_rows(a[rows], e8m0.scales(ea[rows]), w[e], e8m0.scales(ew[e]))
+        assert np.array_equal(bf16_decode(got[rows]), ref), (e, K)
+    assert not got[~inside].any()
+    # fused against GEMM + activation on the same 320-row tiles (N = 2I)
+    I = N // 2
+    od, cd = dev(offsets.astype(np.int32)), dev(counts.astype(np.int32))
+    ad, sad = dev(a), dev(np.ascontiguousarray(as_words(e8m0.pack(ea)).T))
+    wd, swd = dev(w), dev(as_words(e8m0.pack(ew)))
+    nw = (I // 128 + 3) // 4
+    h = torch.zeros(R, N, dtype=torch.bfloat16, device="cuda")
+    q, qs = (torch.zeros(R, I, dtype=torch.uint8, device="cuda"),
+             torch.zeros(nw, R, dtype=torch.int32, device="cuda"))
+    qf, qfs = q.clone(), qs.clone()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fre.moe_grouped_gemm_fp8_e8m0(ad, sad, wd, swd, od, cd, h, st)
+    fre.moe_act_requant_e8m0(h, od, cd, q, qs, st)
+    fre.moe_gate_up_act_fp8_e8m0(ad, sad, wd, swd, od, cd, qf, qfs, st)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    assert np.array_equal(host(qf), host(q)) and np.array_equal(host(qfs), host(qs))
+
+
 ALL = [1, 2, 3, 4, 5]
 
 
