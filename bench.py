@@ -226,6 +226,9 @@ def main():
     ap.add_argument("--zipf", type=float, default=1.0,
                     help="Zipf exponent of the per-expert load (the EP48 decode share, "
                          "--config 3); 1.0 is the workload's, 0.613 gives hottest = 3x coldest")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="copy the routed rows into the permuted buffer in the dispatch "
+                         "(default: the gate/up GEMM gathers them from x in its tile loads)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip measuring the copy and MFMA ceilings")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -292,7 +295,8 @@ def main():
     w_d = torch.from_numpy(w).to(dev)
     rows = cfg.capacity if cfg.layout == fre.LAYOUT_MASKED else fre.contiguous_rows(R, E, cfg.align_m)
     layer = fre.MoELayer(E, H, I, T, K, cfg.layout, rows, align_m=cfg.align_m, device=dev,
-                         scale_fmt=args.scales, fuse_act=False if args.unfused else (True if args.fused else "auto"))
+                         scale_fmt=args.scales, fuse_act=False if args.unfused else (True if args.fused else "auto"),
+                         gather=not args.no_gather)
     fused = layer.fuse_act
     torch.cuda.synchronize()
 
@@ -381,7 +385,9 @@ def main():
     flops2 = 2.0 * R * H * I
     flops = flops1 + flops2
     hb, ib = H // 128, I // 128
-    bytes_perm = (T + R) * (H + 4 * hb) + T * K * 4
+    # dispatch: x read once and the routed rows written once (unless the
+    # gate/up GEMM gathers them), scales the same way, routing read
+    bytes_perm = (T + R) * 4 * hb + T * K * 4 + (0 if layer.gather else (T + R) * H)
     bytes_act = R * (4 * I + I + 4 * ib)
     bytes_comb = R * 2 * H + T * 2 * H + T * K * 8
     # GEMM bytes: weights (and scales) of experts with rows, A and its scales, C
@@ -391,7 +397,7 @@ def main():
                 (R * (I + 4 * ib) if fused else R * 2 * I * 2))
     bytes_g2 = live * (H * I + hb * ib * 4) + R * (I + 4 * ib) + R * H * 2
     tflops = flops / (ms * 1e-3) / 1e12
-    launch_key = f"{cfg.name}:R={R}:rows={rows}"
+    launch_key = f"{cfg.name}:R={R}:rows={rows}" + (":gather" if layer.gather else "")
     traffic = stored_traffic(launch_key) if args.scales == "fp32" and fused else None
     kname = "gate/up GEMM + activation (fused)" if fused else "grouped_gemm_fp8 (gate/up)"
     pct = lambda q: round(float(np.percentile(step_ms, q)), 4)
@@ -415,7 +421,9 @@ def main():
                    "topk": K, "routed_rows": R, "buffer_rows": layer.rows_total,
                    **({"zipf_s": args.zipf} if args.config == 3 else {}),
                    "experts_with_rows": live, "block_scales": args.scales,
-                   "gate_up_activation": "fused" if fused else "separate calls"},
+                   "gate_up_activation": "fused" if fused else "separate calls",
+                   "row_permutation": ("gathered by the gate/up GEMM's tile loads (x[row_src])"
+                                       if layer.gather else "copied by the dispatch")},
         "timing": {"mode": "hipgraph replay" if graph is not None else "eager launches",
                    "cache_flush_mib": args.flush_mib,
                    "step_ms_p10": pct(10), "step_ms_p50": pct(50), "step_ms_p90": pct(90),

@@ -9,6 +9,8 @@ from .ops import (moe_layout_workspace_bytes, moe_gemm_large_tiles, moe_gemm_til
                   moe_quantize_fp8, moe_quantize_fp8_e8m0, moe_dispatch_layout_e8m0,
                   moe_grouped_gemm_fp8_e8m0, moe_act_requant_e8m0,
                   moe_gate_up_act_fp8, moe_gate_up_act_fp8_e8m0,
+                  moe_grouped_gemm_fp8_gather, moe_grouped_gemm_fp8_gather_e8m0,
+                  moe_gate_up_act_fp8_gather, moe_gate_up_act_fp8_gather_e8m0,
                   moe_ceiling_copy, moe_ceiling_mfma_fp8,
                   LAYOUT_CONTIGUOUS, LAYOUT_MASKED,
                   ERR_BAD_EXPERT, ERR_OVERFLOW, ERR_BAD_INDEX)

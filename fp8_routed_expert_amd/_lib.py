@@ -54,11 +54,23 @@ SIGNATURES = {
         _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_quantize_fp8": (ctypes.c_int32, [
         _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_grouped_gemm_fp8_gather": (ctypes.c_int32, [
+        _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+        _vp]),
+    "moe_grouped_gemm_fp8_gather_e8m0": (ctypes.c_int32, [
+        _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+        _vp]),
+    "moe_gate_up_act_fp8_gather": (ctypes.c_int32, [
+        _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+        _vp, _vp]),
+    "moe_gate_up_act_fp8_gather_e8m0": (ctypes.c_int32, [
+        _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+        _vp, _vp]),
     "moe_ceiling_copy": (ctypes.c_int32, [_vp, _vp, _size, _vp]),
     "moe_ceiling_mfma_fp8": (ctypes.c_int32, [_c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lib = None
 

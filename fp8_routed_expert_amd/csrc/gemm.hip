@@ -117,20 +117,22 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint8_t* lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(voff), "s"(r) : "memory", "m0");
 }
-// The same with the offset split into a per-lane part and a wave-uniform
-// part added inside the asm: the compiler cannot then hoist one offset
-// register per chunk out of the K loop (the address is read when the load
-// issues, so the temporary is free right after).
+// The same with the offset split into a per-lane part, XOR-ed with a
+// wave-uniform 0 or 16 (the chunk permutation of the odd 8-row half of a
+// 16-row group), and a wave-uniform part, combined inside the asm: the
+// compiler cannot then hoist one offset register per chunk (or per parity)
+// out of the K loop (the address is read when the load issues, so the
+// temporary is free right after).
 __device__ __forceinline__ void dma16_split(v4i rsrc, uint8_t* lds, uint32_t vlane,
-                                            uint32_t suni) {
+                                            uint32_t sxor, uint32_t suni) {
   const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
   v4i r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
   uint32_t t;
-  asm volatile("v_add_u32_e32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\t"
-               "buffer_load_dwordx4 %0, %4, 0 offen lds"
-               : "=&v"(t) : "s"(suni), "v"(vlane), "s"(m), "s"(r) : "memory", "m0");
+  asm volatile("v_xor_b32_e32 %0, %1, %2\n\tv_add_u32_e32 %0, %3, %0\n\ts_mov_b32 m0, %4\n\t"
+               "buffer_load_dwordx4 %0, %5, 0 offen lds"
+               : "=&v"(t) : "s"(sxor), "v"(vlane), "s"(suni), "s"(m), "s"(r) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -306,13 +308,17 @@ __device__ __forceinline__ void find_mtile(const int32_t* offsets, const int32_t
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2>
+// kGather: A is not the permuted buffer but the source rows x [src_rows, K];
+// buffer row r of the tile is read from x[row_src[r]] (a row with no source
+// reads zero), so the row permutation happens in the tile loads.
+template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2, bool kGather>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, const float* __restrict__ SW,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
     int E, int rows_total, int N, int K, uint16_t* __restrict__ C,
-    uint8_t* __restrict__ Q, void* __restrict__ QS, int32_t* __restrict__ status) {
+    uint8_t* __restrict__ Q, void* __restrict__ QS, int32_t* __restrict__ status,
+    const int32_t* __restrict__ row_src, int src_rows) {
   constexpr int NWM = BM / WM;
   constexpr int NWN = BN / WN;
   constexpr int NW = NWM * NWN;
@@ -394,12 +400,42 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   const int Ih = N / 2;                        // fused: intermediate size
   const int ni0 = tile_n * (BN / 2);           // fused: first intermediate column
 
-  const uint32_t lane_row = (uint32_t)(lane >> 3) * (uint32_t)K;
-  const uint32_t lane_off0 = lane_row + (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4);
-  const uint32_t lane_off1 = lane_row + (uint32_t)(((lane & 7) ^ swz(8 + (lane >> 3))) << 4);
-  const long long a_bytes = (long long)(rows_total - row0) * K;
-  const v4i rsrc_a = make_rsrc(A + (size_t)row0 * K,
+  // Loads that a step issues past the last k-block (live = false) take an
+  // offset beyond every descriptor's range: they read zero without touching
+  // memory, and every step issues the same loads and ends with the same
+  // wait, with no branch in the step (a branch per wait left the compiler's
+  // control flow with paths no execution takes).
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  // A lane's offset in an 8-row DMA chunk: row lane / 8, 16-byte piece
+  // (lane & 7) permuted as that row sits in the even 8-row half of its
+  // 16-row group; in the odd half the permutation differs by XOR 1 on the
+  // piece index, i.e. XOR 16 on the offset (K is a multiple of 128, so the
+  // row part leaves bit 4 alone).
+  const uint32_t lane_off = (uint32_t)(lane >> 3) * (uint32_t)K +
+                            (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4);
+  const long long a_bytes = kGather ? (long long)src_rows * K : (long long)(rows_total - row0) * K;
+  const v4i rsrc_a = make_rsrc(kGather ? A : A + (size_t)row0 * K,
                                (uint32_t)(a_bytes > 0x7ffff000LL ? 0x7ffff000LL : a_bytes));
+  // kGather: per-lane byte offsets of the wave's A chunks in x (chunk u
+  // holds tile rows 8 (wave CA + u) .. + 7, the lane row lane / 8 of them),
+  // read before any tile load; rows without a source get an offset out of
+  // range and load zero.
+  uint32_t a_off[kGather ? CA : 1];
+  if constexpr (kGather) {
+#pragma unroll
+    for (int u = 0; u < CA; ++u) {
+      const int c = wave * CA + u;
+      const int r = row0 + c * 8 + (lane >> 3);
+      const int src = r < rows_total ? row_src[r] : -1;
+      a_off[u] = (src >= 0 && src < src_rows)
+                     ? (uint32_t)src * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz(lane >> 3)) << 4)
+                     : kOutOfRange;   // (the odd-half XOR 16 is applied at issue)
+    }
+    // the offsets (and so the compiler's wait for row_src) are ready before
+    // the first tile load is issued
+#pragma unroll
+    for (int u = 0; u < CA; ++u) asm volatile("" : "+v"(a_off[u]));
+  }
   // fused: the descriptor spans the expert's whole W13 (the host checks
   // N * K < 2^31); the gate and up rows of a tile are two separate runs
   const v4i rsrc_b = kFused ? make_rsrc(W + (size_t)e_sel * N * K, (uint32_t)(N * K))
@@ -437,12 +473,6 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // filled when its load completes, not when the instruction issues, so
   // fs_raw is read only after the wait_loads() that covers these loads,
   // which is also where the compiler sees the values being written.
-  // Loads that a step issues past the last k-block (live = false) take an
-  // offset beyond every descriptor's range: they read zero without touching
-  // memory, and every step issues the same loads and ends with the same
-  // wait, with no branch in the step (a branch per wait left the compiler's
-  // control flow with paths no execution takes).
-  constexpr uint32_t kOutOfRange = 0x80000000u;
   auto load_scales = [&](int kb, bool live) {
     const uint32_t base =
         live ? ((uint32_t)(kPow2 ? kb >> 2 : kb) * (uint32_t)rows_total + srow) * 4u : kOutOfRange;
@@ -453,10 +483,15 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   };
   auto issue_a1 = [&](int kb, uint8_t* tA, int u, bool live) {
     const int c = wave * CA + u;   // wave-uniform; with CA even its parity is u's
-    const bool odd = CA % 2 == 0 ? (u & 1) : (c & 1);
-    dma16_split(rsrc_a, tA + c * 1024, odd ? lane_off1 : lane_off0,
-                __builtin_amdgcn_readfirstlane(
-                    live ? (uint32_t)(c * 8) * (uint32_t)K + (uint32_t)kb * kBK : kOutOfRange));
+    const uint32_t odd16 = (CA % 2 == 0 ? (u & 1) : (c & 1)) ? 16u : 0u;
+    if constexpr (kGather)   // (an out-of-range offset plus kOutOfRange may wrap
+                             // to a small one: a read inside x into a free stage)
+      dma16_split(rsrc_a, tA + c * 1024, a_off[u], __builtin_amdgcn_readfirstlane(odd16),
+                  __builtin_amdgcn_readfirstlane(live ? (uint32_t)kb * kBK : kOutOfRange));
+    else
+      dma16_split(rsrc_a, tA + c * 1024, lane_off, __builtin_amdgcn_readfirstlane(odd16),
+                  __builtin_amdgcn_readfirstlane(
+                      live ? (uint32_t)(c * 8) * (uint32_t)K + (uint32_t)kb * kBK : kOutOfRange));
   };
   auto issue_a = [&](int kb, uint8_t* tA, bool live) {
 #pragma unroll
@@ -485,7 +520,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
         const int wv = row / WN, k = row - wv * WN;
         row = (k < WN / 2 ? 0 : Ih - WN / 2) + ni0 + wv * (WN / 2) + k;
       }
-      dma16_split(rsrc_b, tB + c * 1024, (u & 1) ? lane_off1 : lane_off0,
+      dma16_split(rsrc_b, tB + c * 1024, lane_off, (u & 1) ? 16u : 0u,
                   __builtin_amdgcn_readfirstlane(live ? (uint32_t)row * (uint32_t)K + kofs
                                                       : kOutOfRange));
     }
@@ -859,12 +894,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2 = false>
+template <int BM, int BN, int WM, int WN, int GM, int kTag, bool kPow2 = false, bool kGather = false>
 static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t* w,
                            const float* w_scale, const int32_t* offsets,
                            const int32_t* counts, int E, int rows_total, int N, int K,
                            uint16_t* c, hipStream_t st, int32_t* status,
-                           uint8_t* q = nullptr, void* q_scale = nullptr) {
+                           uint8_t* q = nullptr, void* q_scale = nullptr,
+                           const int32_t* row_src = nullptr, int src_rows = 0) {
   if (N % BN != 0) return MOE_UNSUPPORTED_SHAPE;
   long long m_tiles = kTag == 3 ? ((long long)rows_total + BM - 1) / BM
                                 : (long long)rows_total / BM + E;
@@ -872,9 +908,10 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
   constexpr int threads = 64 * (BM / WM) * (BN / WN);
-  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag, kPow2>),
+  hipLaunchKernelGGL((grouped_gemm_fp8_kernel<BM, BN, WM, WN, GM, kTag, kPow2, kGather>),
                      dim3((unsigned)blocks), dim3(threads), 0, st, a, a_scale, w, w_scale,
-                     offsets, counts, E, rows_total, N, K, c, q, q_scale, status);
+                     offsets, counts, E, rows_total, N, K, c, q, q_scale, status, row_src,
+                     src_rows);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
@@ -943,20 +980,49 @@ static bool scale_span_ok(long long rows_total, int K, bool pow2) {
   return kb * rows_total * 4 <= 0x7ffff000LL;
 }
 
-template <bool kPow2>
+// Gathered A (the *_gather calls): x [src_rows, K] must lie within one
+// buffer descriptor's 32-bit range, and every row of the buffer names its
+// source row in row_src (-1: none).
+static moe_status_t gather_args_ok(const uint8_t* x, int src_rows, const int32_t* row_src,
+                                   int K) {
+  if (src_rows < 0) return MOE_INVALID_ARG;
+  if (!row_src || (src_rows > 0 && !x)) return MOE_INVALID_ARG;
+  if ((long long)src_rows * K > 0x7ffff000LL) return MOE_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+template <bool kPow2, bool kGather = false>
 static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const uint8_t* w,
                                  const float* w_scale, const int32_t* offsets,
                                  const int32_t* counts, int E, int rows_total, int N, int K,
-                                 uint16_t* c, int32_t* status, void* stream) {
+                                 uint16_t* c, int32_t* status, void* stream,
+                                 const int32_t* row_src = nullptr, int src_rows = 0) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || N <= 0 || K <= 0)
     return MOE_INVALID_ARG;
   if (N % kBlock != 0 || K % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
   if (!scale_span_ok(rows_total, K, kPow2)) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts || !w || !w_scale) return MOE_INVALID_ARG;
+  if (kGather) {
+    const moe_status_t g = gather_args_ok(a, src_rows, row_src, K);
+    if (g != MOE_OK) return g;
+  }
   if (rows_total == 0) return MOE_OK;
-  if (!a || !a_scale || !c) return MOE_INVALID_ARG;
+  if ((!kGather && !a) || !a_scale || !c) return MOE_INVALID_ARG;
   if (((uintptr_t)a | (uintptr_t)w | (uintptr_t)c) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if constexpr (kGather) {   // the gate/up projection's symbol, whatever the shape
+    if (kPow2 && use_huge_tiles(rows_total, N, E))
+      return launch<MOE_GEMM_HUGE, 1, true, true>(a, a_scale, w, w_scale, offsets, counts, E,
+                                                  rows_total, N, K, c, st, status, nullptr,
+                                                  nullptr, row_src, src_rows);
+    if (use_big_tiles(rows_total, N, E))
+      return launch<MOE_GEMM_BIG, 1, kPow2, true>(a, a_scale, w, w_scale, offsets, counts, E,
+                                                  rows_total, N, K, c, st, status, nullptr,
+                                                  nullptr, row_src, src_rows);
+    return launch<MOE_GEMM_SMALL, 1, kPow2, true>(a, a_scale, w, w_scale, offsets, counts, E,
+                                                  rows_total, N, K, c, st, status, nullptr,
+                                                  nullptr, row_src, src_rows);
+  }
   const bool gate_up = K > N;   // gate/up: K = H > N = 2I; down: N = H > K = I
   // host-known sizes only, so the choice is the same inside graph capture
   const bool big = use_big_tiles(rows_total, N, E);
@@ -1007,33 +1073,42 @@ extern "C" moe_status_t moe_grouped_gemm_fp8_e8m0(
                             rows_total, N, K, c, status_dev, stream);
 }
 
-template <bool kPow2>
+template <bool kPow2, bool kGather = false>
 static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const uint8_t* w13,
                                 const float* w13_scale, const int32_t* offsets,
                                 const int32_t* counts, int E, int rows_total, int I, int H,
-                                uint8_t* q2, void* q2_scale, int32_t* status, void* stream) {
+                                uint8_t* q2, void* q2_scale, int32_t* status, void* stream,
+                                const int32_t* row_src = nullptr, int src_rows = 0) {
   if (E <= 0 || E > MOE_MAX_EXPERTS || rows_total < 0 || I <= 0 || H <= 0)
     return MOE_INVALID_ARG;
   if (I % kBlock != 0 || H % kBK != 0) return MOE_UNSUPPORTED_SHAPE;
   if (2LL * I * H > 0x7ffff000LL) return MOE_UNSUPPORTED_SHAPE;   // one expert's W13 < 2 GB
   if (!scale_span_ok(rows_total, H, kPow2)) return MOE_UNSUPPORTED_SHAPE;
   if (!offsets || !counts || !w13 || !w13_scale) return MOE_INVALID_ARG;
+  if (kGather) {
+    const moe_status_t g = gather_args_ok(a, src_rows, row_src, H);
+    if (g != MOE_OK) return g;
+  }
   if (rows_total == 0) return MOE_OK;
-  if (!a || !a_scale || !q2 || !q2_scale) return MOE_INVALID_ARG;
+  if ((!kGather && !a) || !a_scale || !q2 || !q2_scale) return MOE_INVALID_ARG;
   if (((uintptr_t)a | (uintptr_t)w13 | (uintptr_t)q2) & 15) return MOE_UNSUPPORTED_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int N = 2 * I;
   // the same host-side rule as the unfused gate/up GEMM
   const bool big = use_big_tiles(rows_total, N, E);
-  if (kPow2 && use_huge_tiles(rows_total, N, E))
+  // (gathered: the per-lane source offsets do not fit beside the 320-row
+  // tile's accumulators and fused epilogue, so that call keeps 256 rows)
+  if (kPow2 && !kGather && use_huge_tiles(rows_total, N, E))
     return launch<MOE_GEMM_HUGE, 4, true>(a, a_scale, w13, w13_scale, offsets, counts, E,
                                           rows_total, N, H, nullptr, st, status, q2, q2_scale);
   if (big)
-    return launch<MOE_GEMM_BIG, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
-                                          rows_total, N, H, nullptr, st, status, q2, q2_scale);
-  return launch<MOE_GEMM_FUSED_SMALL, 4, kPow2>(a, a_scale, w13, w13_scale, offsets, counts, E,
-                                                rows_total, N, H, nullptr, st, status, q2,
-                                                q2_scale);
+    return launch<MOE_GEMM_BIG, 4, kPow2, kGather>(a, a_scale, w13, w13_scale, offsets, counts,
+                                                   E, rows_total, N, H, nullptr, st, status, q2,
+                                                   q2_scale, row_src, src_rows);
+  return launch<MOE_GEMM_FUSED_SMALL, 4, kPow2, kGather>(a, a_scale, w13, w13_scale, offsets,
+                                                         counts, E, rows_total, N, H, nullptr,
+                                                         st, status, q2, q2_scale, row_src,
+                                                         src_rows);
 }
 
 extern "C" moe_status_t moe_gate_up_act_fp8(const uint8_t* a, const float* a_scale,
@@ -1055,6 +1130,42 @@ extern "C" moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_
   return gate_up_act<true>(a, reinterpret_cast<const float*>(a_scale), w13,
                            reinterpret_cast<const float*>(w13_scale), offsets, counts, E,
                            rows_total, I, H, q2, q2_scale, status_dev, stream);
+}
+
+extern "C" moe_status_t moe_grouped_gemm_fp8_gather(
+    const uint8_t* x, int T, const int32_t* row_src, const float* a_scale, const uint8_t* w,
+    const float* w_scale, const int32_t* offsets, const int32_t* counts, int E, int rows_total,
+    int N, int K, uint16_t* c, int32_t* status_dev, void* stream) {
+  return grouped_gemm<false, true>(x, a_scale, w, w_scale, offsets, counts, E, rows_total, N, K,
+                                   c, status_dev, stream, row_src, T);
+}
+
+extern "C" moe_status_t moe_grouped_gemm_fp8_gather_e8m0(
+    const uint8_t* x, int T, const int32_t* row_src, const uint32_t* a_scale, const uint8_t* w,
+    const uint32_t* w_scale, const int32_t* offsets, const int32_t* counts, int E,
+    int rows_total, int N, int K, uint16_t* c, int32_t* status_dev, void* stream) {
+  return grouped_gemm<true, true>(x, reinterpret_cast<const float*>(a_scale), w,
+                                  reinterpret_cast<const float*>(w_scale), offsets, counts, E,
+                                  rows_total, N, K, c, status_dev, stream, row_src, T);
+}
+
+extern "C" moe_status_t moe_gate_up_act_fp8_gather(
+    const uint8_t* x, int T, const int32_t* row_src, const float* a_scale, const uint8_t* w13,
+    const float* w13_scale, const int32_t* offsets, const int32_t* counts, int E,
+    int rows_total, int I, int H, uint8_t* q2, float* q2_scale, int32_t* status_dev,
+    void* stream) {
+  return gate_up_act<false, true>(x, a_scale, w13, w13_scale, offsets, counts, E, rows_total, I,
+                                  H, q2, q2_scale, status_dev, stream, row_src, T);
+}
+
+extern "C" moe_status_t moe_gate_up_act_fp8_gather_e8m0(
+    const uint8_t* x, int T, const int32_t* row_src, const uint32_t* a_scale,
+    const uint8_t* w13, const uint32_t* w13_scale, const int32_t* offsets,
+    const int32_t* counts, int E, int rows_total, int I, int H, uint8_t* q2,
+    uint32_t* q2_scale, int32_t* status_dev, void* stream) {
+  return gate_up_act<true, true>(x, reinterpret_cast<const float*>(a_scale), w13,
+                                 reinterpret_cast<const float*>(w13_scale), offsets, counts, E,
+                                 rows_total, I, H, q2, q2_scale, status_dev, stream, row_src, T);
 }
 
 extern "C" moe_status_t moe_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* w,

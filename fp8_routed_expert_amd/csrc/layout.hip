@@ -441,8 +441,10 @@ static moe_status_t dispatch(
   if ((long long)T * K > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
   if (workspace_bytes < moe_layout_workspace_bytes(T, K, E))
     return MOE_INVALID_ARG;
-  if (T > 0 && (!topk_idx || !x || !x_scale || !slot_of)) return MOE_INVALID_ARG;
-  if (rows_total > 0 && (!row_src || !row_expert || !a || !a_scale))
+  // a == nullptr: the rows are not copied (the *_gather GEMM calls read them
+  // from x through row_src); indices and permuted scales are still written
+  if (T > 0 && (!topk_idx || (a && !x) || !x_scale || !slot_of)) return MOE_INVALID_ARG;
+  if (rows_total > 0 && (!row_src || !row_expert || !a_scale))
     return MOE_INVALID_ARG;
   if (((uintptr_t)x | (uintptr_t)a) & 15) return MOE_UNSUPPORTED_SHAPE;
 
@@ -473,7 +475,7 @@ static moe_status_t dispatch(
     const int pieces = (n16 + 64 * kPermChunks - 1) / (64 * kPermChunks);
     const int plen = (n16 + pieces - 1) / pieces;
     const long long waves = (long long)T * pieces;
-    const long long row_blocks = (waves + 3) / 4;
+    const long long row_blocks = a ? (waves + 3) / 4 : 0;
     const long long scale_blocks = (rows_total + kScTile - 1) / kScTile;
     if (row_blocks + scale_blocks > 0x7fffffffLL) return MOE_UNSUPPORTED_SHAPE;
     hipLaunchKernelGGL(permute_kernel, dim3((unsigned)(row_blocks + scale_blocks)), dim3(256),

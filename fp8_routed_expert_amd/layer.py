@@ -21,6 +21,13 @@ captured into a hipGraph (torch.cuda.CUDAGraph) and replayed.
 scale_fmt "fp32" keeps fp32 block scales; "e8m0" uses packed power-of-two
 scales (int32 words of four biased exponents; the *_e8m0 calls), in which
 case x_scale and the weight scales passed in must be packed the same way.
+
+gather=True (the default) skips the copy of the routed rows into a permuted
+buffer: the dispatch writes the indices and the permuted scales only, and the
+gate/up call reads buffer row r from x[row_src[r]] in its tile loads (the
+*_gather calls; bit-identical results).  The x passed to dispatch() must
+then stay unchanged until the gate/up call has run.  gather=False copies the
+rows into `a` (moe_dispatch_layout's full permute).
 """
 
 import torch
@@ -41,12 +48,16 @@ def big_gate_up_tiles(rows_total, I, E):
 
 class MoELayer:
     def __init__(self, E, H, I, T, K, layout, rows, align_m=128, device="cuda",
-                 scale_fmt="fp32", fuse_act="auto"):
+                 scale_fmt="fp32", fuse_act="auto", gather=True):
         """rows: M_cap for the contiguous layout, capacity C for masked."""
         if scale_fmt not in ("fp32", "e8m0"):
             raise ValueError(f"scale_fmt {scale_fmt!r}")
         if fuse_act not in ("auto", True, False):
             raise ValueError(f"fuse_act {fuse_act!r}")
+        if gather not in (True, False):
+            raise ValueError(f"gather {gather!r}")
+        self.gather = gather
+        self._x = None
         self.scale_fmt = scale_fmt
         self.E, self.H, self.I, self.T, self.K = E, H, I, T, K
         self.layout, self.rows, self.align_m = layout, rows, align_m
@@ -61,7 +72,7 @@ class MoELayer:
         self.slot_of = torch.zeros(T, K, **i32)
         self.row_src = torch.zeros(R, **i32)
         self.row_expert = torch.zeros(R, **i32)
-        self.a = torch.zeros(R, H, dtype=torch.uint8, device=d)
+        self.a = None if gather else torch.zeros(R, H, dtype=torch.uint8, device=d)
         pk = scale_fmt == "e8m0"
         sdt = torch.int32 if pk else torch.float32
         self.a_scale = torch.zeros((H // 128 + 3) // 4 if pk else H // 128, R, dtype=sdt,
@@ -84,16 +95,34 @@ class MoELayer:
         f(topk_idx, x, x_scale, self.E, self.layout, self.align_m, self.rows, self.counts,
           self.offsets, self.slot_of, self.row_src, self.row_expert, self.a, self.a_scale,
           self.workspace, self.status, stream)
+        self._x = x   # the gathered gate/up call reads the rows from here
 
     def gemm1(self, w13, s13, stream=None):
         """Unfused path: h = gate/up GEMM (needs fuse_act=False)."""
         if self.h is None:
             raise RuntimeError("gemm1/act are the unfused path: build with fuse_act=False")
+        if self.gather:
+            f = (ops.moe_grouped_gemm_fp8_gather_e8m0 if self.scale_fmt == "e8m0"
+                 else ops.moe_grouped_gemm_fp8_gather)
+            f(self._source(), self.row_src, self.a_scale, w13, s13, self.offsets, self.counts,
+              self.h, self.status, stream)
+            return
         self._gemm(self.a, self.a_scale, w13, s13, self.offsets, self.counts, self.h,
                    self.status, stream)
 
+    def _source(self):
+        if self._x is None:
+            raise RuntimeError("the gathered gate/up call needs dispatch() first")
+        return self._x
+
     def gemm1_act(self, w13, s13, stream=None):
         """Fused path: q2, q2_scale straight from the gate/up GEMM."""
+        if self.gather:
+            f = (ops.moe_gate_up_act_fp8_gather_e8m0 if self.scale_fmt == "e8m0"
+                 else ops.moe_gate_up_act_fp8_gather)
+            f(self._source(), self.row_src, self.a_scale, w13, s13, self.offsets, self.counts,
+              self.q2, self.q2_scale, self.status, stream)
+            return
         f = (ops.moe_gate_up_act_fp8_e8m0 if self.scale_fmt == "e8m0"
              else ops.moe_gate_up_act_fp8)
         f(self.a, self.a_scale, w13, s13, self.offsets, self.counts, self.q2, self.q2_scale,

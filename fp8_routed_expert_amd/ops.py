@@ -67,7 +67,8 @@ def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
     """Count / prefix-sum / stably rank / permute the routed rows.
 
     rows is M_cap (contiguous) or the per-expert capacity C (masked);
-    a is [rows_total, H], a_scale [H/128, rows_total] (K-block-major)."""
+    a is [rows_total, H], a_scale [H/128, rows_total] (K-block-major).
+    a=None: the rows are not copied (for the *_gather GEMM calls)."""
     T, K = topk_idx.shape
     H = x.shape[1]
     rows_total = E * rows if layout == LAYOUT_MASKED else rows
@@ -80,7 +81,7 @@ def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,
         _ptr(slot_of, _I32, "slot_of", (T, K)),
         _ptr(row_src, _I32, "row_src", (rows_total,)),
         _ptr(row_expert, _I32, "row_expert", (rows_total,)),
-        _ptr(a, _U8, "a", (rows_total, H)),
+        None if a is None else _ptr(a, _U8, "a", (rows_total, H)),
         _ptr(a_scale, _F32, "a_scale", (H // 128, rows_total)),
         _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
         _ptr(status, _I32, "status", (1,)), _stream(stream))
@@ -105,7 +106,7 @@ def moe_dispatch_layout_noalloc(topk_idx, x, x_scale, E, layout, align_m, rows, 
         _ptr(slot_of, _I32, "slot_of", (T, K)),
         _ptr(row_src, _I32, "row_src", (rows_total,)),
         _ptr(row_expert, _I32, "row_expert", (rows_total,)),
-        _ptr(a, _U8, "a", (rows_total, H)),
+        None if a is None else _ptr(a, _U8, "a", (rows_total, H)),
         _ptr(a_scale, _F32, "a_scale", (H // 128, rows_total)),
         _ptr(status, _I32, "status", (1,)), _stream(stream))
     check(st, "moe_dispatch_layout_noalloc")
@@ -176,6 +177,74 @@ def moe_gate_up_act_fp8_e8m0(a, a_scale, w13, w13_scale, offsets, counts, q2, q2
     q2_scale [ceil(I/512), rows_total]."""
     _gate_up_act("moe_gate_up_act_fp8_e8m0", a, a_scale, w13, w13_scale, offsets, counts, q2,
                  q2_scale, status, stream, True)
+
+
+def _grouped_gemm_gather(name, x, row_src, a_scale, w, w_scale, offsets, counts, c, status,
+                         stream, packed):
+    E, N, K = w.shape
+    T = x.shape[0]
+    rows_total = row_src.numel()
+    kw = _words(K // 128) if packed else K // 128
+    sdt = _I32 if packed else _F32
+    lib = load()
+    st = getattr(lib, name)(
+        _ptr(x, _U8, "x", (T, K)), T, _ptr(row_src, _I32, "row_src", (rows_total,)),
+        _ptr(a_scale, sdt, "a_scale", (kw, rows_total)), _ptr(w, _U8, "w", (E, N, K)),
+        _ptr(w_scale, sdt, "w_scale", (E, N // 128, kw)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)), _ptr(counts, _I32, "counts", (E,)),
+        E, rows_total, N, K, _ptr(c, _BF16, "c", (rows_total, N)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, name)
+
+
+def moe_grouped_gemm_fp8_gather(x, row_src, a_scale, w, w_scale, offsets, counts, c, status,
+                                stream=None):
+    """moe_grouped_gemm_fp8 reading buffer row r from x[row_src[r]] (x [T, K]
+    e4m3; a row without a source reads zero) instead of a permuted buffer."""
+    _grouped_gemm_gather("moe_grouped_gemm_fp8_gather", x, row_src, a_scale, w, w_scale,
+                         offsets, counts, c, status, stream, False)
+
+
+def moe_grouped_gemm_fp8_gather_e8m0(x, row_src, a_scale, w, w_scale, offsets, counts, c,
+                                     status, stream=None):
+    """moe_grouped_gemm_fp8_gather with packed scales."""
+    _grouped_gemm_gather("moe_grouped_gemm_fp8_gather_e8m0", x, row_src, a_scale, w, w_scale,
+                         offsets, counts, c, status, stream, True)
+
+
+def _gate_up_act_gather(name, x, row_src, a_scale, w13, w13_scale, offsets, counts, q2,
+                        q2_scale, status, stream, packed):
+    E, I2, H = w13.shape
+    I = I2 // 2
+    T = x.shape[0]
+    rows_total = row_src.numel()
+    sdt = _I32 if packed else _F32
+    hw = _words(H // 128) if packed else H // 128
+    iw = _words(I // 128) if packed else I // 128
+    lib = load()
+    st = getattr(lib, name)(
+        _ptr(x, _U8, "x", (T, H)), T, _ptr(row_src, _I32, "row_src", (rows_total,)),
+        _ptr(a_scale, sdt, "a_scale", (hw, rows_total)),
+        _ptr(w13, _U8, "w13", (E, I2, H)), _ptr(w13_scale, sdt, "w13_scale", (E, I2 // 128, hw)),
+        _ptr(offsets, _I32, "offsets", (E + 1,)), _ptr(counts, _I32, "counts", (E,)),
+        E, rows_total, I, H, _ptr(q2, _U8, "q2", (rows_total, I)),
+        _ptr(q2_scale, sdt, "q2_scale", (iw, rows_total)),
+        _ptr(status, _I32, "status", (1,)), _stream(stream))
+    check(st, name)
+
+
+def moe_gate_up_act_fp8_gather(x, row_src, a_scale, w13, w13_scale, offsets, counts, q2,
+                               q2_scale, status, stream=None):
+    """moe_gate_up_act_fp8 reading buffer row r from x[row_src[r]]."""
+    _gate_up_act_gather("moe_gate_up_act_fp8_gather", x, row_src, a_scale, w13, w13_scale,
+                        offsets, counts, q2, q2_scale, status, stream, False)
+
+
+def moe_gate_up_act_fp8_gather_e8m0(x, row_src, a_scale, w13, w13_scale, offsets, counts, q2,
+                                    q2_scale, status, stream=None):
+    """moe_gate_up_act_fp8_gather with packed scales."""
+    _gate_up_act_gather("moe_gate_up_act_fp8_gather_e8m0", x, row_src, a_scale, w13,
+                        w13_scale, offsets, counts, q2, q2_scale, status, stream, True)
 
 
 def moe_act_requant(h, offsets, counts, q, q_scale, status, stream=None):
@@ -261,7 +330,7 @@ def moe_dispatch_layout_e8m0(topk_idx, x, x_scale, E, layout, align_m, rows, cou
         _ptr(slot_of, _I32, "slot_of", (T, K)),
         _ptr(row_src, _I32, "row_src", (rows_total,)),
         _ptr(row_expert, _I32, "row_expert", (rows_total,)),
-        _ptr(a, _U8, "a", (rows_total, H)),
+        None if a is None else _ptr(a, _U8, "a", (rows_total, H)),
         _ptr(a_scale, _I32, "a_scale", (hw, rows_total)),
         _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(),
         _ptr(status, _I32, "status", (1,)), _stream(stream))

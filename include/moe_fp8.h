@@ -126,7 +126,10 @@ int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales);
  *   slot_of   [T, K]   permuted row of each (t, k); -1 = none / dropped
  *   row_src   [rows_total]  source token of each row, -1 if no entry
  *   row_expert[rows_total]  expert of each row, -1 if no entry
- *   a         [rows_total, H] e4m3   a[slot] = x[row_src[slot]]
+ *   a         [rows_total, H] e4m3   a[slot] = x[row_src[slot]]; may be
+ *             NULL: the rows are then not copied (the *_gather calls read
+ *             them from x through row_src) and x may be NULL too; indices
+ *             and a_scale are written as usual
  *   a_scale   [H/128, rows_total] f32 (K-block-major) matching scales
  *   workspace moe_layout_workspace_bytes(T, K, E) bytes of device memory
  * Rows of one expert are ordered by flat index t*K + k.  Rows that do not
@@ -370,6 +373,45 @@ moe_status_t moe_gate_up_act_fp8_e8m0(const uint8_t* a, const uint32_t* a_scale,
                                       int E, int rows_total, int I, int H,
                                       uint8_t* q2, uint32_t* q2_scale,
                                       int32_t* status_dev, void* stream);
+
+/*
+ * The gate/up calls with the permutation of the rows done in their tile
+ * loads [H100-EP 基于 DeepEP 的专家并行 and DeepGEMM 集成: the routed rows
+ * grouped per expert feed the grouped GEMM]: instead of the permuted buffer
+ * `a`, they take the source rows x [T, K] e4m3 (K = H, the contraction
+ * width) and row_src [rows_total] (as moe_dispatch_layout writes it) and
+ * read buffer row r from x[row_src[r]]; a row with row_src < 0 or >= T is
+ * read as zero.  The row scales are the permuted a_scale as before (so the
+ * dispatch can run with a == NULL).  Results equal the plain calls on the
+ * permuted buffer bit for bit.  Extra checks: T < 0, row_src NULL, or x NULL
+ * with T > 0 -> MOE_INVALID_ARG; T * K > 0x7ffff000 bytes (one buffer
+ * descriptor) -> MOE_UNSUPPORTED_SHAPE.  Otherwise as the plain calls; the
+ * fused packed-scale form keeps 256-row tiles where the others use 320.
+ */
+moe_status_t moe_grouped_gemm_fp8_gather(const uint8_t* x, int T, const int32_t* row_src,
+                                         const float* a_scale, const uint8_t* w,
+                                         const float* w_scale, const int32_t* offsets,
+                                         const int32_t* counts, int E, int rows_total,
+                                         int N, int K, uint16_t* c, int32_t* status_dev,
+                                         void* stream);
+moe_status_t moe_grouped_gemm_fp8_gather_e8m0(const uint8_t* x, int T, const int32_t* row_src,
+                                              const uint32_t* a_scale, const uint8_t* w,
+                                              const uint32_t* w_scale, const int32_t* offsets,
+                                              const int32_t* counts, int E, int rows_total,
+                                              int N, int K, uint16_t* c, int32_t* status_dev,
+                                              void* stream);
+moe_status_t moe_gate_up_act_fp8_gather(const uint8_t* x, int T, const int32_t* row_src,
+                                        const float* a_scale, const uint8_t* w13,
+                                        const float* w13_scale, const int32_t* offsets,
+                                        const int32_t* counts, int E, int rows_total, int I,
+                                        int H, uint8_t* q2, float* q2_scale,
+                                        int32_t* status_dev, void* stream);
+moe_status_t moe_gate_up_act_fp8_gather_e8m0(const uint8_t* x, int T, const int32_t* row_src,
+                                             const uint32_t* a_scale, const uint8_t* w13,
+                                             const uint32_t* w13_scale, const int32_t* offsets,
+                                             const int32_t* counts, int E, int rows_total,
+                                             int I, int H, uint8_t* q2, uint32_t* q2_scale,
+                                             int32_t* status_dev, void* stream);
 
 /*
  * Measurement helpers (not steps of the layer).  They time the two

@@ -154,3 +154,32 @@ def test_gemm_tile_rule():
     assert rows(13135, 2048, 3, 1) == 320    # the synthetic 320-row test shape
     assert rows(4096, 4096, 32, 1) == 128
     assert rows(0, 4096, 1, 1) == -1
+
+
+def test_gather_argument_checks():
+    """The *_gather calls refuse a missing row_src, a negative source-row
+    count, a null x with rows to read (MOE_INVALID_ARG) and an x beyond one
+    buffer descriptor's 32-bit range (MOE_UNSUPPORTED_SHAPE) before any
+    launch; with valid arguments but a null output they fail on that
+    (INVALID_ARG), so the gather checks come first."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(4096)
+    H, I, N2 = 7168, 2048, 4096
+    big_T = 0x7ffff000 // H + 1
+    for f in (lib.moe_grouped_gemm_fp8_gather, lib.moe_grouped_gemm_fp8_gather_e8m0):
+        #        x     T      row_src a_scale w  w_scale offs  counts E rows   N   K  c  st  stream
+        assert f(fake, 100, N, fake, fake, fake, fake, fake, 4, 256, N2, H, fake, fake, N) == 1
+        assert f(fake, -1, fake, fake, fake, fake, fake, fake, 4, 256, N2, H, fake, fake, N) == 1
+        assert f(N, 100, fake, fake, fake, fake, fake, fake, 4, 256, N2, H, fake, fake, N) == 1
+        assert f(fake, big_T, fake, fake, fake, fake, fake, fake, 4, 256, N2, H, fake, fake,
+                 N) == 2
+        assert f(fake, big_T - 1, fake, fake, fake, fake, fake, fake, 4, 256, N2, H, N, fake,
+                 N) == 1
+    for f in (lib.moe_gate_up_act_fp8_gather, lib.moe_gate_up_act_fp8_gather_e8m0):
+        #        x     T    row_src a_scale w13 w13_s offs  counts E rows  I  H  q2  q2s   st  stream
+        assert f(fake, 100, N, fake, fake, fake, fake, fake, 4, 256, I, H, fake, fake, fake,
+                 N) == 1
+        assert f(fake, big_T, fake, fake, fake, fake, fake, fake, 4, 256, I, H, fake, fake,
+                 fake, N) == 2
+        assert f(fake, big_T - 1, fake, fake, fake, fake, fake, fake, 4, 256, I, H, N, fake,
+                 fake, N) == 1

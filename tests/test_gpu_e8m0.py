@@ -47,7 +47,7 @@ def test_dispatch_e8m0_moves_packed_words(gpu):
     cfg = inp["cfg"]
     rows = rows_for(cfg, inp["idx"])
     layer = fre.MoELayer(cfg.E, cfg.H, cfg.I, cfg.T, cfg.K, cfg.layout, rows,
-                         align_m=cfg.align_m, scale_fmt="e8m0")
+                         align_m=cfg.align_m, scale_fmt="e8m0", gather=False)
     layer.dispatch(dev(inp["idx"]), dev(inp["x"]), dev(inp["xp"]))
     torch.cuda.synchronize()
     L = moe.dispatch_layout(inp["idx"], cfg.E, cfg.layout, align_m=cfg.align_m, rows=rows)

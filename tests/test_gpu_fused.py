@@ -66,7 +66,7 @@ def test_fused_equals_gemm_then_act(gpu, cid, fmt):
     cfg = inp["cfg"]
     rows = rows_for(cfg, inp["idx"])
     layer = fre.MoELayer(cfg.E, cfg.H, cfg.I, cfg.T, cfg.K, cfg.layout, rows,
-                         align_m=cfg.align_m, scale_fmt=fmt)
+                         align_m=cfg.align_m, scale_fmt=fmt, gather=False)
     layer.dispatch(dev(inp["idx"]), dev(inp["x"]), dev(inp["xp"] if packed else inp["xs"]))
     w13 = dev(inp["w13"])
     s13 = dev(inp["p13"] if packed else inp["s13"])
