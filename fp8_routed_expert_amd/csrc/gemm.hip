@@ -935,6 +935,12 @@ static moe_status_t launch(const uint8_t* a, const float* a_scale, const uint8_t
 #ifndef MOE_GEMM_HUGE
 #define MOE_GEMM_HUGE 320, 256, 160, 64, 2
 #endif
+// Decode shares whose large tiles fit one round on the CUs: 192 x 256 tiles
+// of 8 waves of 96 x 64, as long as they still fit one round (fewer fed
+// bytes per k-step: 56 KB instead of 64 KB).
+#ifndef MOE_GEMM_MID
+#define MOE_GEMM_MID 192, 256, 96, 64, 2
+#endif
 // The fused gate/up + activation kernel needs a tile to cover one whole
 // 1x128 block of intermediate columns (BN = 256: 128 gate + 128 up
 // columns): large problems use MOE_GEMM_BIG, small ones 128 x 256 tiles of
@@ -964,6 +970,32 @@ static bool use_big_tiles(long long rows_total, int N, int E) {
 static bool use_huge_tiles(long long rows_total, int N, int E) {
   return use_big_tiles(rows_total, N, E) && rows_total >= 4096LL * E &&
          (rows_total / 320) * (N / 256) >= 256;
+}
+
+// One round of workgroups: the tile count the GPU runs at once (one large
+// tile per CU of an MI355X).
+constexpr long long kRoundTiles = 256;
+
+// Tiles of height BM for a buffer of rows_total rows in E segments, read as
+// a contiguous buffer with 128-row alignment (M_cap = R + 127 E): R / BM plus
+// half a partial tile per expert.  An estimate for the host-side rule only:
+// the grid is sized by the exact bound in launch().
+static long long est_tiles(long long rows_total, int N, int E, int BM) {
+  long long r = rows_total - 127LL * E;
+  if (r <= 0) r = rows_total;
+  return ((r + BM - 1) / BM + (E + 1) / 2) * (N / 256);
+}
+
+// 192-row tiles: only where the 256-row tiles already fit one round, and
+// the 192-row tiles still do -- then every tile starts at once either way and
+// each moves 1/8 fewer bytes per k-step.  Measured at the EP72 decode share
+// (gate/up: 10 m-tiles of 256, 13 of 192, x 16 n-tiles): gate/up GEMM 104 ->
+// 91 us, fused with the activation 116 -> 99 us, bit-identical; where the
+// 192-row tiles need a second round (its down GEMM, the EP48 share) they were
+// 13-30% slower, hence the rule.
+static bool use_mid_tiles(long long rows_total, int N, int E) {
+  return use_big_tiles(rows_total, N, E) && est_tiles(rows_total, N, E, 256) <= kRoundTiles &&
+         est_tiles(rows_total, N, E, 192) <= kRoundTiles;
 }
 
 }  // namespace moe
@@ -1015,6 +1047,10 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
       return launch<MOE_GEMM_HUGE, 1, true, true>(a, a_scale, w, w_scale, offsets, counts, E,
                                                   rows_total, N, K, c, st, status, nullptr,
                                                   nullptr, row_src, src_rows);
+    if (use_mid_tiles(rows_total, N, E))
+      return launch<MOE_GEMM_MID, 1, kPow2, true>(a, a_scale, w, w_scale, offsets, counts, E,
+                                                  rows_total, N, K, c, st, status, nullptr,
+                                                  nullptr, row_src, src_rows);
     if (use_big_tiles(rows_total, N, E))
       return launch<MOE_GEMM_BIG, 1, kPow2, true>(a, a_scale, w, w_scale, offsets, counts, E,
                                                   rows_total, N, K, c, st, status, nullptr,
@@ -1030,6 +1066,11 @@ static moe_status_t grouped_gemm(const uint8_t* a, const float* a_scale, const u
     return gate_up ? launch<MOE_GEMM_HUGE, 1, true>(a, a_scale, w, w_scale, offsets, counts,
                                                     E, rows_total, N, K, c, st, status)
                    : launch<MOE_GEMM_HUGE, 2, true>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st, status);
+  if (use_mid_tiles(rows_total, N, E))
+    return gate_up ? launch<MOE_GEMM_MID, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
+                                                    E, rows_total, N, K, c, st, status)
+                   : launch<MOE_GEMM_MID, 2, kPow2>(a, a_scale, w, w_scale, offsets, counts,
                                                     E, rows_total, N, K, c, st, status);
   if (big)
     return gate_up ? launch<MOE_GEMM_BIG, 1, kPow2>(a, a_scale, w, w_scale, offsets, counts,
@@ -1052,6 +1093,7 @@ static constexpr int tile_rows(int bm, int, int, int, int) { return bm; }
 extern "C" int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales) {
   if (rows_total <= 0 || N <= 0 || E <= 0) return -1;
   if (packed_scales && use_huge_tiles(rows_total, N, E)) return tile_rows(MOE_GEMM_HUGE);
+  if (use_mid_tiles(rows_total, N, E)) return tile_rows(MOE_GEMM_MID);
   return use_big_tiles(rows_total, N, E) ? tile_rows(MOE_GEMM_BIG) : tile_rows(MOE_GEMM_SMALL);
 }
 
@@ -1101,6 +1143,10 @@ static moe_status_t gate_up_act(const uint8_t* a, const float* a_scale, const ui
   if (kPow2 && !kGather && use_huge_tiles(rows_total, N, E))
     return launch<MOE_GEMM_HUGE, 4, true>(a, a_scale, w13, w13_scale, offsets, counts, E,
                                           rows_total, N, H, nullptr, st, status, q2, q2_scale);
+  if (use_mid_tiles(rows_total, N, E))
+    return launch<MOE_GEMM_MID, 4, kPow2, kGather>(a, a_scale, w13, w13_scale, offsets, counts,
+                                                   E, rows_total, N, H, nullptr, st, status, q2,
+                                                   q2_scale, row_src, src_rows);
   if (big)
     return launch<MOE_GEMM_BIG, 4, kPow2, kGather>(a, a_scale, w13, w13_scale, offsets, counts,
                                                    E, rows_total, N, H, nullptr, st, status, q2,

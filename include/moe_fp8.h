@@ -90,7 +90,7 @@ size_t moe_layout_workspace_bytes(int T, int K, int E);
 /* Whether the grouped GEMM calls (moe_grouped_gemm_fp8, moe_gate_up_act_fp8,
  * their _e8m0 forms; N = 2I for the gate/up projection) and moe_gemm_fp8
  * (E = 1, rows_total = M) run a problem of this size with large tiles (1:
- * 256 x 256, or 320 x 256 for the _e8m0 calls at the sizes where
+ * 256 x 256, or 320 x 256 or 192 x 256 at the sizes where
  * moe_gemm_tile_rows says so) or small ones (0: 128 x 128; 128 x 256 for
  * the fused gate/up + activation).  A host-side rule of the sizes alone, so
  * it is the same under graph capture; the rule itself is stated where it is
@@ -98,10 +98,13 @@ size_t moe_layout_workspace_bytes(int T, int K, int E);
  * choose between the fused and the separate gate/up + activation calls. */
 int moe_gemm_large_tiles(long long rows_total, int N, int E);
 
-/* The row height of the output tiles those calls use for this size: 320,
- * 256 or 128.  packed_scales != 0 asks about the _e8m0 calls (the only ones
- * with 320-row tiles), 0 about the fp32-scale calls.  -1 for negative or
- * zero sizes. */
+/* The row height of the output tiles the grouped calls use for this size:
+ * 320, 256, 192 or 128.  packed_scales != 0 asks about the _e8m0 calls (the
+ * only ones with 320-row tiles, which the gathered fused call does not take:
+ * it keeps 256 there), 0 about the fp32-scale calls.  192 marks the sizes
+ * whose large tiles fit one round on the CUs either way (decode shares).
+ * moe_gemm_fp8 always uses 256 rows when moe_gemm_large_tiles is 1.  -1 for
+ * negative or zero sizes. */
 int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales);
 
 /*

@@ -153,6 +153,12 @@ def test_gemm_tile_rule():
     assert rows(6906, 4096, 6, 1) == 256     # decode: segments under 4096 rows
     assert rows(13135, 2048, 3, 1) == 320    # the synthetic 320-row test shape
     assert rows(4096, 4096, 32, 1) == 128
+    # one round either way: EP72 decode gate/up (10 x 16 tiles of 256 rows,
+    # 13 x 16 of 192) takes 192 rows; its down projection (N = 7168: 280
+    # tiles of 256) and the EP48 share (432 tiles) keep 256
+    assert rows(2556, 4096, 4, 0) == 192 and rows(2556, 4096, 4, 1) == 192
+    assert rows(2556, 7168, 4, 0) == 256
+    assert rows(6906, 4096, 6, 0) == 256
     assert rows(0, 4096, 1, 1) == -1
 
 

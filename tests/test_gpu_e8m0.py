@@ -94,6 +94,56 @@ def test_gemm_e8m0_exact_integers(gpu):
             assert np.array_equal(bf16_decode(got[s:en]), ref), e
 
 
+def _run_gemm_fp32(a, sa_rows, w, sw, offsets, counts):
+    E, N, K = w.shape
+    c = torch.zeros(a.shape[0], N, dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fre.moe_grouped_gemm_fp8(dev(a), dev(np.ascontiguousarray(sa_rows.T)), dev(w), dev(sw),
+                             dev(offsets.astype(np.int32)), dev(counts.astype(np.int32)), c, st)
+    torch.cuda.synchronize()
+    return host(c)
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["fp32", "e8m0"])
+def test_gemm_exact_integers_192_row_tiles(gpu, packed):
+    """The 192 x 256 tiles (taken when the large tiles fit one round on the
+    CUs either way) on exact small-integer data with power-of-two scales, in
+    both scale formats: a 5-row expert, an empty one and a long one whose
+    last tile straddles its end (4700 = 24 x 192 + 92).  Sampled rows (segment
+    ends, every tile boundary, random rows) equal the oracle bit for bit and
+    rows outside the segments are never written."""
+    g = np.random.default_rng(53 + packed)
+    E, N, K = 3, 2048, 384
+    counts = np.array([5, 0, 4700])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    R = int(offsets[-1]) + 7
+    assert fre.moe_gemm_tile_rows(R, N, E, packed) == 192
+    a = e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float64))
+    w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
+    ea = g.integers(-2, 3, (R, K // 128)).astype(np.int32)
+    ew = g.integers(-2, 3, (E, N // 128, K // 128)).astype(np.int32)
+    log(f"192-row tiles: R={R} N={N} K={K} E={E} packed={packed}")
+    if packed:
+        got = _run_gemm_e8m0(a, ea, w, ew, offsets, counts)
+    else:
+        got = _run_gemm_fp32(a, np.ldexp(1.0, ea).astype(np.float32), w,
+                             np.ldexp(1.0, ew).astype(np.float32), offsets, counts)
+    inside = np.zeros(R, bool)
+    for e in range(E):
+        s, en = int(offsets[e]), int(offsets[e] + counts[e])
+        if en <= s:
+            continue
+        inside[s:en] = True
+        rows = {s, en - 1}
+        rows |= {r for t in range(1, (en - s) // 192 + 1) for r in (s + 192 * t - 1, s + 192 * t)
+                 if r < en}
+        rows |= set(g.integers(s, en, 24).tolist())
+        rows = np.array(sorted(rows))
+        ref = moe.gemm_rows(a[rows], e8m0.scales(ea[rows]), w[e], e8m0.scales(ew[e]))
+        assert np.array_equal(bf16_decode(got[rows]), ref), e
+    assert not got[~inside].any()
+
+
 @pytest.mark.parametrize("K", [128, 384, 640])
 def test_gemm_e8m0_exact_integers_320_row_tiles(gpu, K):
     """The 320 x 256 tiles of the packed path (two A stages) on exact

@@ -95,26 +95,32 @@ def test_gather_equals_permuted(gpu, cid, fmt):
 
 
 @pytest.mark.parametrize("packed", [False, True], ids=["fp32", "e8m0"])
-@pytest.mark.parametrize("shape", ["small", "rows320"])
+@pytest.mark.parametrize("shape", ["small", "rows320", "rows192"])
 def test_gather_edge_rows(gpu, packed, shape):
     """Unaligned segments, an empty expert, and rows whose source is -1 or
     past the last source row inside a segment: the gathered GEMM equals the
     plain GEMM on a buffer built on the host (a[r] = x[row_src[r]], zero
     for a missing source), so a missing source reads zero; the gathered fused
     call equals the plain fused call on that buffer.  "rows320" is a shape
-    where the packed-scale GEMM runs its 320-row tiles."""
+    where the packed-scale GEMM runs its 320-row tiles, "rows192" one where
+    both formats run 192-row tiles."""
     g = np.random.default_rng(41 + packed)
     if shape == "small":
         E, I, H, T = 3, 256, 640, 300
         counts = np.array([37, 0, 200])
-    else:
+    elif shape == "rows320":
         E, I, H, T = 3, 1024, 384, 9000
         counts = np.array([5, 0, 13123])
+    else:
+        E, I, H, T = 3, 1024, 384, 3000
+        counts = np.array([5, 0, 4700])
     N = 2 * I
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1]) + 7
     if packed and shape == "rows320":
         assert fre.moe_gemm_tile_rows(R, N, E, True) == 320
+    if shape == "rows192":
+        assert fre.moe_gemm_tile_rows(R, N, E, packed) == 192
     x = e4m3_encode(g.standard_normal((T, H)))
     row_src = np.full(R, -1, np.int32)
     row_src[: offsets[-1]] = g.integers(0, T, int(offsets[-1]))
