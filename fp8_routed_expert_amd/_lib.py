@@ -24,7 +24,7 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "moe_layout_workspace_bytes": (_size, [_c_int, _c_int, _c_int]),
     "moe_gemm_large_tiles": (_c_int, [ctypes.c_longlong, _c_int, _c_int]),
-    "moe_gemm_tile_rows": (_c_int, [ctypes.c_longlong, _c_int, _c_int, _c_int]),
+    "moe_gemm_tile_rows": (_c_int, [ctypes.c_longlong, _c_int, _c_int, _c_int, _c_int]),
     "moe_dispatch_layout": (ctypes.c_int32, [
         _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp, _vp]),
@@ -70,7 +70,7 @@ SIGNATURES = {
     "moe_ceiling_mfma_fp8": (ctypes.c_int32, [_c_int, _c_int, _vp, _vp, _vp]),
 }
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _lib = None
 

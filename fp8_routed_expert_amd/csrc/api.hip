@@ -1,7 +1,7 @@
 // Library-wide entry points of libmoe_fp8 that launch no kernel.
 #include "moe_fp8.h"
 
-extern "C" int moe_abi_version(void) { return 8; }
+extern "C" int moe_abi_version(void) { return 9; }
 
 extern "C" const char* moe_status_string(moe_status_t status) {
   switch (status) {

@@ -54,11 +54,12 @@ def moe_gemm_large_tiles(rows_total, N, E):
     return int(load().moe_gemm_large_tiles(int(rows_total), int(N), int(E)))
 
 
-def moe_gemm_tile_rows(rows_total, N, E, packed_scales=False):
-    """Row height (320, 256 or 128) of the output tiles the GEMM calls use
-    for this size; packed_scales for the *_e8m0 calls.  -1 for
-    non-positive sizes."""
-    return int(load().moe_gemm_tile_rows(int(rows_total), int(N), int(E), int(bool(packed_scales))))
+def moe_gemm_tile_rows(rows_total, N, K, E, packed_scales=False):
+    """Row height (320, 256, 192, 128 or 64) of the output tiles the
+    grouped GEMM calls use for N outputs over K inputs at this size;
+    packed_scales for the *_e8m0 calls.  -1 for non-positive sizes."""
+    return int(load().moe_gemm_tile_rows(int(rows_total), int(N), int(K), int(E),
+                                         int(bool(packed_scales))))
 
 
 def moe_dispatch_layout(topk_idx, x, x_scale, E, layout, align_m, rows, counts,

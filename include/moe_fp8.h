@@ -91,21 +91,26 @@ size_t moe_layout_workspace_bytes(int T, int K, int E);
  * their _e8m0 forms; N = 2I for the gate/up projection) and moe_gemm_fp8
  * (E = 1, rows_total = M) run a problem of this size with large tiles (1:
  * 256 x 256, or 320 x 256 or 192 x 256 at the sizes where
- * moe_gemm_tile_rows says so) or small ones (0: 128 x 128; 128 x 256 for
- * the fused gate/up + activation).  A host-side rule of the sizes alone, so
+ * moe_gemm_tile_rows says so) or small ones (0: 128 x 128, or 64 x 128
+ * where moe_gemm_tile_rows says 64; 128 x 256 for the fused gate/up +
+ * activation).  A host-side rule of the sizes alone, so
  * it is the same under graph capture; the rule itself is stated where it is
  * implemented.  Returns -1 for negative or zero sizes.  Callers use it to
  * choose between the fused and the separate gate/up + activation calls. */
 int moe_gemm_large_tiles(long long rows_total, int N, int E);
 
-/* The row height of the output tiles the grouped calls use for this size:
- * 320, 256, 192 or 128.  packed_scales != 0 asks about the _e8m0 calls (the
- * only ones with 320-row tiles, which the gathered fused call does not take:
- * it keeps 256 there), 0 about the fp32-scale calls.  192 marks the sizes
- * whose large tiles fit one round on the CUs either way (decode shares).
- * moe_gemm_fp8 always uses 256 rows when moe_gemm_large_tiles is 1.  -1 for
- * negative or zero sizes. */
-int moe_gemm_tile_rows(long long rows_total, int N, int E, int packed_scales);
+/* The row height of the output tiles the grouped calls use for a product
+ * of N outputs over K inputs (gate/up: N = 2I, K = H; down: N = H, K = I):
+ * 320, 256, 192, 128 or 64.  packed_scales != 0 asks about the _e8m0 calls
+ * (the only ones with 320-row tiles, which the gathered fused call does not
+ * take: it keeps 256 there), 0 about the fp32-scale calls.  192 marks the
+ * sizes whose large tiles fit one round on the CUs either way (decode
+ * shares); 64 the gate/up products (K > N) of buffers with at most 128 rows
+ * per expert on small tiles (the masked decode layout), which the
+ * moe_grouped_gemm_fp8 calls run with 64-row tiles and the fused call with
+ * its 128 x 256 ones.  moe_gemm_fp8 always uses 256 rows when
+ * moe_gemm_large_tiles is 1.  -1 for negative or zero sizes. */
+int moe_gemm_tile_rows(long long rows_total, int N, int K, int E, int packed_scales);
 
 /*
  * moe_dispatch_layout — count, prefix-sum, stably rank and permute the

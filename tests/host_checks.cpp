@@ -39,8 +39,10 @@ int main() {
   expect("workspace bytes", moe_layout_workspace_bytes(2048, 8, 32) > 0, 1);
   expect("large tiles invalid", moe_gemm_large_tiles(0, 4096, 1), -1);
   expect("large tiles prefill", moe_gemm_large_tiles(132183, 4096, 9), 1);
-  expect("tile rows packed prefill", moe_gemm_tile_rows(132183, 7168, 9, 1), 320);
-  expect("tile rows masked", moe_gemm_tile_rows(4096, 4096, 32, 0), 128);
+  expect("tile rows packed prefill", moe_gemm_tile_rows(132183, 7168, 2048, 9, 1), 320);
+  expect("tile rows masked gate/up", moe_gemm_tile_rows(4096, 4096, 7168, 32, 0), 64);
+  expect("tile rows masked down", moe_gemm_tile_rows(4096, 7168, 2048, 32, 0), 128);
+  expect("tile rows invalid K", moe_gemm_tile_rows(4096, 7168, 0, 32, 0), -1);
 
   // dispatch: topk, x, x_scale, T, K, E, H, layout, align_m, rows, counts,
   // offsets, slot_of, row_src, row_expert, a, a_scale, workspace, bytes, status, stream

@@ -147,19 +147,23 @@ def test_gemm_tile_rule():
     assert f(2048, 4096, 1) == 0        # dense, 8 x 16 = 128: not more than half the CUs
     assert f(0, 4096, 1) == -1 and f(256, 0, 1) == -1 and f(256, 256, 0) == -1
     rows = lib.moe_gemm_tile_rows
-    assert rows(132183, 4096, 9, 1) == 320   # prefill share, packed scales
-    assert rows(132183, 7168, 9, 1) == 320
-    assert rows(132183, 4096, 9, 0) == 256   # fp32 scales keep 256 x 256
-    assert rows(6906, 4096, 6, 1) == 256     # decode: segments under 4096 rows
-    assert rows(13135, 2048, 3, 1) == 320    # the synthetic 320-row test shape
-    assert rows(4096, 4096, 32, 1) == 128
+    H, I = 7168, 2048
+    assert rows(132183, 2 * I, H, 9, 1) == 320   # prefill share, packed scales
+    assert rows(132183, H, I, 9, 1) == 320
+    assert rows(132183, 2 * I, H, 9, 0) == 256   # fp32 scales keep 256 x 256
+    assert rows(6906, 2 * I, H, 6, 1) == 256     # decode: segments under 4096 rows
+    assert rows(13135, 2048, 384, 3, 1) == 320   # the synthetic 320-row test shape
+    # masked layout, capacity 128: 64-row tiles for gate/up, 128 for down
+    assert rows(4096, 2 * I, H, 32, 1) == 64 and rows(4096, 2 * I, H, 32, 0) == 64
+    assert rows(4096, H, I, 32, 1) == 128 and rows(4096, H, I, 32, 0) == 128
+    assert rows(636, 256, 256, 4, 0) == 128      # tiny: 159 rows per expert
     # one round either way: EP72 decode gate/up (10 x 16 tiles of 256 rows,
     # 13 x 16 of 192) takes 192 rows; its down projection (N = 7168: 280
     # tiles of 256) and the EP48 share (432 tiles) keep 256
-    assert rows(2556, 4096, 4, 0) == 192 and rows(2556, 4096, 4, 1) == 192
-    assert rows(2556, 7168, 4, 0) == 256
-    assert rows(6906, 4096, 6, 0) == 256
-    assert rows(0, 4096, 1, 1) == -1
+    assert rows(2556, 2 * I, H, 4, 0) == 192 and rows(2556, 2 * I, H, 4, 1) == 192
+    assert rows(2556, H, I, 4, 0) == 256
+    assert rows(6906, 2 * I, H, 6, 0) == 256
+    assert rows(0, 4096, H, 1, 1) == -1 and rows(256, 4096, 0, 1, 1) == -1
 
 
 def test_gather_argument_checks():

@@ -117,7 +117,7 @@ def test_gemm_exact_integers_192_row_tiles(gpu, packed):
     counts = np.array([5, 0, 4700])
     offsets = np.concatenate([[0], np.cumsum(counts)])
     R = int(offsets[-1]) + 7
-    assert fre.moe_gemm_tile_rows(R, N, E, packed) == 192
+    assert fre.moe_gemm_tile_rows(R, N, K, E, packed) == 192
     a = e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float64))
     w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
     ea = g.integers(-2, 3, (R, K // 128)).astype(np.int32)
@@ -158,7 +158,7 @@ def test_gemm_e8m0_exact_integers_320_row_tiles(gpu, K):
     counts = np.array([5, 0, 13123])
     offsets = np.concatenate([[0], np.cumsum(counts)])
     R = int(offsets[-1]) + 7
-    assert fre.moe_gemm_tile_rows(R, N, E, True) == 320
+    assert fre.moe_gemm_tile_rows(R, N, K, E, True) == 320
     a = e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float64))
     w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
     ea = g.integers(-2, 3, (R, K // 128)).astype(np.int32)

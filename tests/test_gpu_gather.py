@@ -118,9 +118,9 @@ def test_gather_edge_rows(gpu, packed, shape):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1]) + 7
     if packed and shape == "rows320":
-        assert fre.moe_gemm_tile_rows(R, N, E, True) == 320
+        assert fre.moe_gemm_tile_rows(R, N, H, E, True) == 320
     if shape == "rows192":
-        assert fre.moe_gemm_tile_rows(R, N, E, packed) == 192
+        assert fre.moe_gemm_tile_rows(R, N, H, E, packed) == 192
     x = e4m3_encode(g.standard_normal((T, H)))
     row_src = np.full(R, -1, np.int32)
     row_src[: offsets[-1]] = g.integers(0, T, int(offsets[-1]))

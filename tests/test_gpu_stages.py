@@ -241,17 +241,21 @@ def _run_gemm(a, sa_rows, w, sw, offsets, counts, rows_total):
     return host(c)
 
 
-def test_gemm_exact_integers_pow2_scales(gpu):
+@pytest.mark.parametrize("tile_rows,tail", [(64, 3), (128, 240)])
+def test_gemm_exact_integers_pow2_scales(gpu, tile_rows, tail):
     """Small-integer codes and power-of-two scales keep every sum exact, so
     the device result must equal the oracle's bit for bit: with codes in
     [-4, 4] and scales 2^[-2, 2] every partial sum is a multiple of 2^-4
     below 2^17, exact in fp32 in any summation order.  Segments are
-    unaligned, one expert is empty, and tiles straddle segment ends."""
+    unaligned, one expert is empty, and tiles straddle segment ends.  The
+    rows after the last segment decide the tile height (at most 128 buffer
+    rows per expert: 64-row tiles; more: 128)."""
     g = np.random.default_rng(21)
     E, N, K = 4, 384, 512
     counts = np.array([37, 0, 200, 129])
     offsets = np.concatenate([[0], np.cumsum(counts)])
-    rows_total = int(offsets[-1]) + 3
+    rows_total = int(offsets[-1]) + tail
+    assert fre.moe_gemm_tile_rows(rows_total, N, K, E) == tile_rows
     a = e4m3_encode(g.integers(-4, 5, (rows_total, K)).astype(np.float64))
     w = e4m3_encode(g.integers(-4, 5, (E, N, K)).astype(np.float64))
     sa = np.ldexp(1.0, g.integers(-2, 3, (rows_total, K // 128))).astype(np.float32)
