@@ -12,9 +12,13 @@
 // Design (gfx950):
 //   * Large problems: a workgroup computes a 256 x 256 tile of c with 8 waves
 //     of 128 x 64 (two waves per SIMD, one workgroup per CU, the full 160 KB
-//     of LDS).  Small problems: 128 x 128 tiles of 4 waves of 64 x 64, two
-//     workgroups per CU.  A wave's sub-tile is a grid of 16 x 16 MFMA
-//     subtiles.
+//     of LDS); packed scales at prefill sizes 320 x 256, and decode sizes
+//     whose tiles fit one round on the CUs 192 x 256.  Small problems:
+//     128 x 128 tiles of 4 waves of 64 x 64, two workgroups per CU (64 x 128
+//     for the gate/up projection of the masked decode layout, 128 x 256 for
+//     the fused gate/up + activation).  The host picks the shape from the
+//     sizes alone (rules beside the tile configurations below).  A wave's
+//     sub-tile is a grid of 16 x 16 MFMA subtiles.
 //   * K advances one 128-wide scale block per step.  v_mfma_f32_16x16x128
 //     _f8f6f4 consumes exactly one block per subtile, so each block's raw
 //     product comes out of a single MFMA issued with a zero accumulator and
@@ -973,16 +977,6 @@ static bool use_big_tiles(long long rows_total, int N, int E) {
   return N % 256 == 0 && rows_total >= 256LL * E && (rows_total / 256) * (N / 256) > 128;
 }
 
-// 320-row tiles (packed scales only): a tile then receives 72 KB per k-step
-// for 320 x 256 outputs instead of 64 KB for 256 x 256, 10% fewer bytes per
-// flop through the per-CU feed that bounds the large tiles.  Taken when the
-// segments average at least 4096 rows (the partial last tile of each
-// expert then wastes a few percent at most) and the tiles fill every CU.
-static bool use_huge_tiles(long long rows_total, int N, int E) {
-  return use_big_tiles(rows_total, N, E) && rows_total >= 4096LL * E &&
-         (rows_total / 320) * (N / 256) >= 256;
-}
-
 // One round of workgroups: the tile count the GPU runs at once (one large
 // tile per CU of an MI355X).
 constexpr long long kRoundTiles = 256;
@@ -997,13 +991,6 @@ static long long est_tiles(long long rows_total, int N, int E, int BM) {
   return ((r + BM - 1) / BM + (E + 1) / 2) * (N / 256);
 }
 
-// 192-row tiles: only where the 256-row tiles already fit one round, and
-// the 192-row tiles still do -- then every tile starts at once either way and
-// each moves 1/8 fewer bytes per k-step.  Measured at the EP72 decode share
-// (gate/up: 10 m-tiles of 256, 13 of 192, x 16 n-tiles): gate/up GEMM 104 ->
-// 91 us, fused with the activation 116 -> 99 us, bit-identical; where the
-// 192-row tiles need a second round (its down GEMM, the EP48 share) they were
-// 13-30% slower, hence the rule.
 // 64-row tiles: for the gate/up projection (K > N) when the small tiles run
 // and the segments average at most 128 rows.  A segment of a few dozen rows
 // then fills one 64-row tile instead of padding a 128-row one, and the
@@ -1016,9 +1003,30 @@ static bool use_short_tiles(long long rows_total, int N, int K, int E) {
   return K > N && !use_big_tiles(rows_total, N, E) && rows_total <= 128LL * E;
 }
 
+// 192-row tiles: only where the 256-row tiles already fit one round, and
+// the 192-row tiles still do -- then every tile starts at once either way and
+// each moves 1/8 fewer bytes per k-step.  Measured at the EP72 decode share
+// (gate/up: 10 m-tiles of 256, 13 of 192, x 16 n-tiles): gate/up GEMM 104 ->
+// 91 us, fused with the activation 116 -> 99 us, bit-identical; where the
+// 192-row tiles need a second round (its down GEMM, the EP48 share) they were
+// 13-30% slower, hence the rule.
 static bool use_mid_tiles(long long rows_total, int N, int E) {
   return use_big_tiles(rows_total, N, E) && est_tiles(rows_total, N, E, 256) <= kRoundTiles &&
          est_tiles(rows_total, N, E, 192) <= kRoundTiles;
+}
+
+// 320-row tiles (packed scales only): a tile then receives 72 KB per k-step
+// for 320 x 256 outputs instead of 64 KB for 256 x 256, 10% fewer bytes per
+// flop through the per-CU feed that bounds the large tiles.  Taken when the
+// segments average at least 4096 rows (the partial last tile of each
+// expert then wastes a few percent at most) and the tiles fill every CU.
+// (At the EP72 decode share's down projection, 224 tiles of 320 rows fit one
+// round where 280 of 256 need a second one for the last 24, yet the step
+// measured 3-4% slower with them: each expert's ~512 rows fill 2 x 320 rows
+// at 80%, and each tile is fed 72 KB per k-step instead of 64.)
+static bool use_huge_tiles(long long rows_total, int N, int E) {
+  return use_big_tiles(rows_total, N, E) && rows_total >= 4096LL * E &&
+         (rows_total / 320) * (N / 256) >= 256;
 }
 
 }  // namespace moe

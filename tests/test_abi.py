@@ -162,6 +162,7 @@ def test_gemm_tile_rule():
     # tiles of 256) and the EP48 share (432 tiles) keep 256
     assert rows(2556, 2 * I, H, 4, 0) == 192 and rows(2556, 2 * I, H, 4, 1) == 192
     assert rows(2556, H, I, 4, 0) == 256
+    assert rows(2556, H, I, 4, 1) == 256   # packed too (320 rows measured slower there)
     assert rows(6906, 2 * I, H, 6, 0) == 256
     assert rows(0, 4096, H, 1, 1) == -1 and rows(256, 4096, 0, 1, 1) == -1
 
