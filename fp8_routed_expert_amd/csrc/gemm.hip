@@ -508,9 +508,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void grouped_gemm_fp8_k
   // half lets the first MFMAs start earlier.  Measured at the prefill shape:
   // 0.6-1.9% off the unfused gate/up GEMM and the down GEMM over three boxes
   // (deferring the B rows as well, or having only one wave per SIMD issue
-  // all the tile loads, was slower); the fused kernel keeps the early
-  // issue, with which it needs no register spills.
-  constexpr bool kLateA = !kFused;
+  // all the tile loads, was slower); on the fused gate/up + activation
+  // 1.5% (fp32 scales) and 2.3% (packed) at prefill, 2% and 7% on the EP72
+  // and EP48 decode shares, bit-identical.  The 320-row fused kernel keeps
+  // the early issue: with the late one it spills four registers.
+  constexpr bool kLateA = !kFused || BM < 320;
   // The packed-scale step runs subtile rows 0 .. MI - 2 before its barrier
   // and the fp32 step rows 0 .. MI - 1, so row 1 exists in both once MI >= 3;
   // with MI = 2 the A rows go out after row 0.  (A row index no step reaches
