@@ -3,6 +3,9 @@ include/moe_fp8.h declares, and rejects bad host-side arguments before any
 launch (nothing here touches a GPU)."""
 
 import ctypes
+import os
+import shutil
+import subprocess
 
 import pytest
 
@@ -16,6 +19,20 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++11")])
+def test_header_is_plain_c(lang, std):
+    """The boundary header compiles on its own as C99 and as C++11 with
+    warnings as errors: plain types and pointers only, nothing from HIP or
+    torch."""
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "include", "moe_fp8.h")
+    subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", std, "-x", lang, hdr],
+                   check=True, capture_output=True)
 
 
 def test_version_and_status_strings():
